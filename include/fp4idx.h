@@ -1,0 +1,199 @@
+/*
+ * fp4idx: FP4 lightning-indexer hot path for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libfp4idx.so. Every pointer argument marked "device" is a device address on the
+ * current HIP device; the library never allocates, frees or synchronises. All calls are
+ * asynchronous on `stream` (a hipStream_t; NULL is the legacy default stream) and results are
+ * valid once the stream has reached the call. Arguments are validated on the host before any
+ * HIP call; a failing call returns a negative status, enqueues nothing and records a message
+ * for idx_last_error(). Nothing is thrown or aborted across this boundary.
+ *
+ * Sources, cited by page title and section:
+ *  [P1] "DeepSeek-V4.1 model structure (3): sequence dimension, Hierarchical Sparse Indexer and
+ *       FP4 KV cache" (blog.javazero.top)
+ *  [P3] "DeepSeek-V4 model structure (2): Lightning Indexer and sparse selection" (xhh.club)
+ *
+ * Data layout shared by every entry point ("indexer rows"):
+ *  - an indexer row is one 128-dim vector (a query head or a key) in MXFP4: 64 code bytes, two
+ *    E2M1 codes per byte with element 2i in the low nibble of byte i, plus 4 UE8M0 scale bytes,
+ *    one per group of 32 elements (byte value = exponent + 127) ([P1] "the scale format decides
+ *    precision": groups of 32 with an E8M0 scale, 4.25 bits per element, 68 bytes per key);
+ *  - codes live in one array [rows][64] and scales in another [rows][4];
+ *  - a query is 32 consecutive rows (heads 0..31), weights are fp32 [nq][32].
+ */
+#ifndef FP4IDX_H
+#define FP4IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t idx_status;
+
+#define IDX_OK 0
+#define IDX_EINVAL (-1)        /* null pointer, negative size, inconsistent strides */
+#define IDX_EALIGN (-2)        /* a device pointer is not aligned as documented */
+#define IDX_EUNSUPPORTED (-3)  /* a parameter outside what the kernels implement */
+#define IDX_EHIP (-4)          /* a HIP launch failed; the message names the HIP error */
+#define IDX_EWORKSPACE (-5)    /* workspace missing or smaller than idx_workspace_size() */
+
+#define IDX_ABI_VERSION 1
+
+#define IDX_HEADS 32
+#define IDX_DIM 128
+#define IDX_MAX_K 2048
+
+/* operation codes for idx_workspace_size */
+#define IDX_OP_BUILD_POOL 1
+#define IDX_OP_TOPK 2
+
+/* Version of this ABI (IDX_ABI_VERSION). */
+int32_t idx_abi_version(void);
+
+/* Message of the last failing call on this host thread ("" if none). The string is owned by
+ * the library and stays valid until the next call on the same thread. */
+const char* idx_last_error(void);
+
+/* Bytes of workspace that `op` needs for nq rows of at most max_n values and selection size k
+ * (k = topk_blocks for IDX_OP_BUILD_POOL). Returns 0 for an unknown op or invalid sizes. */
+size_t idx_workspace_size(int32_t op, int32_t nq, int64_t max_n, int32_t k);
+
+/*
+ * idx_quantize_q: random-Hadamard rotation followed by MXFP4 quantisation of 128-dim rows.
+ *
+ * Implements the quantise rule q_c = round_E2M1(x_c / s) with s a power of two ([P1] "E2M1 has
+ * only 15 values" and "the scale format decides precision": the ideal max/6 is rounded up to a
+ * power of two) after the rotation that reduces quantisation error ([P3], Q&A on the indexer's
+ * quantisation). Used for the indexer queries and, with the same math, for the key cache rows.
+ *
+ *   y   = fl32( fl32(S) * fl32(2^-3.5) ),  S_i = sum_c H[i][c] * signs[c] * x[c]  (exact sum),
+ *         H[i][c] = (-1)^popcount(i & c) (Sylvester order);
+ *   e_g = smallest integer with 6 * 2^e_g >= max_{c in group g} |y_c|, clamped to [-127, 127],
+ *         -127 for an all-zero group; scales[g] = e_g + 127;
+ *   code_c = E2M1 of y_c / 2^e_g, round to nearest, ties to the even mantissa bit; zero is +0.
+ *
+ *   x_bf16 : device, bf16 bit patterns [rows][128], 16-byte aligned.
+ *   rows   : number of rows, >= 0 (0 enqueues nothing).
+ *   signs  : device int8 [128], each +1 or -1 (other values give unspecified codes).
+ *   codes  : device uint8 [rows][64], 16-byte aligned (written).
+ *   scales : device uint8 [rows][4], 4-byte aligned (written).
+ * Inputs must be finite and the 128 values of a row must span at most 38 binades (the sum S is
+ * then exact in fp64); otherwise the result is unspecified.
+ */
+idx_status idx_quantize_q(const uint16_t* x_bf16, int64_t rows, const int8_t* signs, uint8_t* codes,
+                          uint8_t* scales, void* stream);
+
+/*
+ * idx_score_full: Full-layer scan. For every query t and visible key position s < n_t:
+ *
+ *   I_{t,s} = sum_{j=0..31} w_{t,j} * ReLU(q_{t,j} . k_s)
+ *
+ * ([P1] "Reindex layers score a million entries per token": the score equation with 32 heads of
+ * 128 dims; [P3] Q&A: ReLU instead of softmax, query-generated weights), with q and k in MXFP4,
+ * per-head dots computed exactly by scaled-FP4 matrix instructions and the head sum in fp32;
+ * fused with the block maxima of the candidate pool, B_b = max_{8b <= s < 8b+8, s < n_t} I_{t,s}
+ * with positions past n_t counting as -inf ([P1] "use shallow-layer scores to limit
+ * deep-layer scoring" and the walk-through of the official pool code). The newest-block pin is
+ * applied by idx_build_pool, not here.
+ *
+ *   k_codes, k_scales : device key cache, [N][64] and [N][4] (16- and 4-byte aligned).
+ *   k_base  : device int64 [nq]; query t reads key rows k_base[t] .. k_base[t] + n_t - 1.
+ *   n_vis   : device int32 [nq]; n_t = min(max(n_vis[t], 0), max_n).
+ *   nq      : number of queries, >= 0.
+ *   group   : >= 1 and divides nq; each run of `group` consecutive queries shares one key range
+ *             (k_base equal within a run): 1 for batched decode, the chunk size for prefill.
+ *   max_n   : host upper bound on n_vis, >= 0 (sizes the launch grid).
+ *   q_codes, q_scales : device, [nq][32][64] and [nq][32][4] (16- and 4-byte aligned).
+ *   w       : device fp32 [nq][32], 4-byte aligned.
+ *   scores  : device fp32 [nq][score_stride] or NULL; written for s < n_t only.
+ *   score_stride : >= max_n when scores or head_dots is given.
+ *   block_max : device fp32 [nq][bm_stride] or NULL; written for b < ceil(n_t / 8) only.
+ *   bm_stride : >= ceil(max_n / 8) when block_max is given.
+ *   head_dots : device fp32 [nq][32][score_stride] or NULL: the per-head dots q_{t,j}.k_s
+ *               (a debugging output; slow).
+ * At least one of scores, block_max, head_dots must be non-NULL.
+ */
+idx_status idx_score_full(const uint8_t* k_codes, const uint8_t* k_scales, const int64_t* k_base,
+                          const int32_t* n_vis, int32_t nq, int32_t group, int64_t max_n, const uint8_t* q_codes,
+                          const uint8_t* q_scales, const float* w, float* scores, int64_t score_stride,
+                          float* block_max, int64_t bm_stride, float* head_dots, void* stream);
+
+/*
+ * idx_build_pool: candidate pool of the Hierarchical Sparse Indexer from the Full layer's block
+ * maxima ([P1] "use shallow-layer scores to limit deep-layer scoring" and "three details of the
+ * pool in the code"): the block holding position n_t - 1 gets +inf, blocks are ranked by
+ * (value desc, block id asc), the first min(topk_blocks, ceil(n_t / block)) are kept (those
+ * whose value is above -inf). With at most topk_blocks blocks every block is kept.
+ *
+ *   block_max  : device fp32 [nq][bm_stride], raw maxima as written by idx_score_full.
+ *   n_vis      : device int32 [nq]; n_t = min(max(n_vis[t], 0), max_n).
+ *   max_n      : host upper bound on n_vis.
+ *   topk_blocks: 1 .. 2048 (2048 in the method).
+ *   block      : must be 8 (the method's block size).
+ *   pool_blocks: device int32 [nq][pool_stride], ascending block ids, -1 after pool_count[t].
+ *   pool_stride: >= topk_blocks.
+ *   pool_count : device int32 [nq] (written).
+ *   ws, ws_bytes : device workspace of at least idx_workspace_size(IDX_OP_BUILD_POOL, nq, max_n,
+ *                  topk_blocks) bytes, 16-byte aligned; its contents need no initialisation and
+ *                  are clobbered. Calls that run concurrently need separate workspaces.
+ */
+idx_status idx_build_pool(const float* block_max, int64_t bm_stride, const int32_t* n_vis, int32_t nq,
+                          int64_t max_n, int32_t topk_blocks, int32_t block, int32_t* pool_blocks,
+                          int64_t pool_stride, int32_t* pool_count, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * idx_score_pool_gather: Reindex-layer scoring restricted to the candidate pool. Only the key
+ * rows of the listed blocks are read and scored with the layer's own q and w ([P1] "use
+ * shallow-layer scores to limit deep-layer scoring": Reindex layers score only pool positions,
+ * 16384 x 4096 MACs per query independent of context length; and the remark that the saving
+ * needs a kernel that reads only pooled keys, after the mask-form reference code).
+ *
+ *   k_codes, k_scales, k_base, n_vis, q_codes, q_scales, w : as for idx_score_full (group 1).
+ *   blocks      : device int32 [nq][blocks_stride]; block ids (any order) of query t are
+ *                 blocks[t][0 .. block_count[t] - 1].
+ *   block_count : device int32 [nq]; values are clamped to [0, max_blocks].
+ *   max_blocks  : host bound, 0 .. 1 << 20.
+ *   block       : must be 8.
+ *   scores      : device fp32 [nq][score_stride], score_stride >= 8 * max_blocks; slot 8 * i + r
+ *                 holds the score of position 8 * blocks[t][i] + r, or -inf when i >=
+ *                 block_count[t] or the position is >= n_t (all 8 * max_blocks slots written).
+ *   head_dots   : device fp32 [nq][32][score_stride] or NULL (debugging output).
+ */
+idx_status idx_score_pool_gather(const uint8_t* k_codes, const uint8_t* k_scales, const int64_t* k_base,
+                                 const int32_t* n_vis, int32_t nq, const int32_t* blocks, int64_t blocks_stride,
+                                 const int32_t* block_count, int32_t max_blocks, int32_t block,
+                                 const uint8_t* q_codes, const uint8_t* q_scales, const float* w, float* scores,
+                                 int64_t score_stride, float* head_dots, void* stream);
+
+/*
+ * idx_topk: the k largest values of each row ([P1] "use shallow-layer scores...": each layer keeps
+ * its own top-512), ranked by (value desc, index asc); -inf (and NaN) values never enter the
+ * selection. Output per row: min(k, number of eligible values) indices in rank order, then -1.
+ *
+ *   scores       : device fp32 [nq][score_stride]; row t uses values 0 .. n_t - 1.
+ *   n_valid      : device int32 [nq] or NULL (NULL means max_n for every row);
+ *                  n_t = min(max(n_valid[t], 0), max_n).
+ *   max_n        : host upper bound, 0 .. 1 << 30.
+ *   k            : 1 .. 2048.
+ *   blocks       : NULL, or a device int32 [nq][blocks_stride] block map as produced by
+ *                  idx_build_pool: value slot s of row t stands for position
+ *                  blocks[t][s / block] * block + s % block, and that position is both the
+ *                  reported index and the tie-break key.
+ *   block        : 8 when blocks is given (ignored otherwise).
+ *   out_idx      : device int32 [nq][out_stride], out_stride >= k.
+ *   out_val      : device fp32 [nq][out_stride] or NULL; -inf after the selected values.
+ *   ws, ws_bytes : at least idx_workspace_size(IDX_OP_TOPK, nq, max_n, k) bytes, 16-byte aligned,
+ *                  clobbered; separate workspaces for concurrent calls.
+ */
+idx_status idx_topk(const float* scores, int64_t score_stride, const int32_t* n_valid, int32_t nq, int64_t max_n,
+                    int32_t k, const int32_t* blocks, int64_t blocks_stride, int32_t block, int32_t* out_idx,
+                    int64_t out_stride, float* out_val, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4IDX_H */

@@ -1,0 +1,157 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol, and rejects
+bad arguments with the documented status before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4idx.h")
+LIB = os.path.join(ROOT, "top_fp4_lightning_amd", "libfp4idx.so")
+
+
+@pytest.fixture(scope="module")
+def fx():
+    if not os.path.exists(LIB):
+        from top_fp4_lightning_amd.build import build_library
+
+        build_library()
+    import top_fp4_lightning_amd
+
+    return top_fp4_lightning_amd
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(idx_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["idx_quantize_q", "idx_score_full", "idx_build_pool", "idx_score_pool_gather", "idx_topk",
+              "idx_last_error", "idx_abi_version", "idx_workspace_size"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(fx):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(fx.lib, n)
+    assert set(fx.EXPORTS) == set(declared_functions())
+
+
+def test_version_and_workspace_sizes(fx):
+    assert fx.abi_version() == 1
+    assert fx.workspace_size(fx.IDX_OP_TOPK, 8, 1 << 20, 512) > 0
+    assert fx.workspace_size(fx.IDX_OP_TOPK, 8, 1 << 20, 512) >= 8 * (1 << 20) * 8
+    assert fx.workspace_size(fx.IDX_OP_BUILD_POOL, 8, 1 << 20, 2048) < fx.workspace_size(fx.IDX_OP_TOPK, 8, 1 << 20,
+                                                                                           2048)
+    assert fx.workspace_size(99, 8, 100, 10) == 0
+    assert fx.workspace_size(fx.IDX_OP_TOPK, 8, 100, 4096) == 0
+    assert fx.workspace_size(fx.IDX_OP_TOPK, -1, 100, 10) == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails first
+
+
+def call(fx, name, *args):
+    st = getattr(fx.lib, name)(*args)
+    return st, fx.lib.idx_last_error().decode()
+
+
+def test_quantize_validation(fx):
+    assert call(fx, "idx_quantize_q", None, -1, None, None, None, None)[0] == fx.IDX_EINVAL
+    assert call(fx, "idx_quantize_q", None, 0, None, None, None, None)[0] == fx.IDX_OK  # empty is a no-op
+    st, msg = call(fx, "idx_quantize_q", None, 5, FAKE, FAKE, FAKE, None)
+    assert st == fx.IDX_EINVAL and "null" in msg
+    st, msg = call(fx, "idx_quantize_q", FAKE + 2, 5, FAKE, FAKE, FAKE, None)
+    assert st == fx.IDX_EALIGN
+
+
+def test_score_full_validation(fx):
+    f = lambda *a: call(fx, "idx_score_full", *a)[0]
+    good = [FAKE, FAKE, FAKE, FAKE, 4, 1, 100, FAKE, FAKE, FAKE, FAKE, 100, FAKE, 13, None, None]
+    bad = list(good); bad[10] = None; bad[12] = None  # no outputs
+    assert f(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[5] = 3  # group does not divide nq
+    assert f(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[11] = 99  # score stride too small
+    assert f(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[13] = 12  # block-max stride too small
+    assert f(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[0] = FAKE + 8  # key codes must be 16-byte aligned
+    assert f(*bad) == fx.IDX_EALIGN
+    bad = list(good); bad[4] = 70000
+    assert f(*bad) == fx.IDX_EUNSUPPORTED
+    bad = list(good); bad[2] = None
+    assert f(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[6] = -5
+    assert f(*bad) == fx.IDX_EINVAL
+
+
+def test_build_pool_validation(fx):
+    ws = fx.workspace_size(fx.IDX_OP_BUILD_POOL, 4, 100, 2048)
+    f = lambda *a: call(fx, "idx_build_pool", *a)[0]
+    good = [FAKE, 13, FAKE, 4, 100, 2048, 8, FAKE, 2048, FAKE, FAKE, ws, None]
+    bad = list(good); bad[6] = 4
+    assert f(*bad) == fx.IDX_EUNSUPPORTED
+    bad = list(good); bad[5] = 4096
+    assert f(*bad) == fx.IDX_EUNSUPPORTED
+    bad = list(good); bad[11] = ws - 1
+    assert f(*bad) == fx.IDX_EWORKSPACE
+    bad = list(good); bad[10] = None
+    assert f(*bad) == fx.IDX_EWORKSPACE
+    bad = list(good); bad[8] = 100
+    assert f(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[10] = FAKE + 4
+    assert f(*bad) == fx.IDX_EALIGN
+
+
+def test_gather_and_topk_validation(fx):
+    g = lambda *a: call(fx, "idx_score_pool_gather", *a)[0]
+    good = [FAKE, FAKE, FAKE, FAKE, 2, FAKE, 2048, FAKE, 2048, 8, FAKE, FAKE, FAKE, FAKE, 16384, None, None]
+    bad = list(good); bad[9] = 16
+    assert g(*bad) == fx.IDX_EUNSUPPORTED
+    bad = list(good); bad[14] = 16383
+    assert g(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[6] = 100
+    assert g(*bad) == fx.IDX_EINVAL
+    ws = fx.workspace_size(fx.IDX_OP_TOPK, 2, 16384, 512)
+    t = lambda *a: call(fx, "idx_topk", *a)[0]
+    good = [FAKE, 16384, None, 2, 16384, 512, None, 0, 8, FAKE, 512, None, FAKE, ws, None]
+    bad = list(good); bad[5] = 0
+    assert t(*bad) == fx.IDX_EUNSUPPORTED
+    bad = list(good); bad[5] = 2049
+    assert t(*bad) == fx.IDX_EUNSUPPORTED
+    bad = list(good); bad[10] = 100
+    assert t(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[13] = ws - 8
+    assert t(*bad) == fx.IDX_EWORKSPACE
+    bad = list(good); bad[6] = FAKE; bad[7] = 10  # block map stride too small
+    assert t(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[6] = FAKE; bad[7] = 2048; bad[8] = 4
+    assert t(*bad) == fx.IDX_EUNSUPPORTED
+
+
+def test_python_binding_refuses_cpu_tensors(fx):
+    import torch
+
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    s = torch.ones(128, dtype=torch.int8)
+    with pytest.raises(ValueError):
+        fx.idx_quantize_q(x, s, torch.empty(4, 64, dtype=torch.uint8), torch.empty(4, 4, dtype=torch.uint8))
+
+
+def test_product_path_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "top_fp4_lightning_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in src and "from oracle" not in src and "liboracle" not in src, fn
+                assert "orc_" not in src, fn

@@ -1,0 +1,240 @@
+"""GPU parity against the CPU oracle (needs an MI355X). Each call goes through the C ABI.
+
+Bar: quantised codes and scales bit-exact; per-head dots bit-exact (whenever the oracle reports
+them exactly representable, which the synthetic recipe always satisfies); scores within 1e-5 of
+A = sum_j |w_j| ReLU(d_j); selections identical except entries within that tolerance of the k-th
+value; selections over identical fp32 inputs identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import (TOL, assert_pool_set, assert_scores_close, assert_topk_set, block_A, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fx():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import top_fp4_lightning_amd
+
+    return top_fp4_lightning_amd
+
+
+@pytest.fixture(scope="module")
+def pl(fx):
+    from top_fp4_lightning_amd import pipeline
+
+    return pipeline
+
+
+def bf16_rows(vals: np.ndarray) -> np.ndarray:
+    return np.array([[synth.bf16_rne(float(v)) for v in row] for row in vals], dtype=np.uint16)
+
+
+def special_rows():
+    rows = []
+    rows.append(np.zeros(128))
+    r = np.random.default_rng(1).standard_normal(128); r[32:64] = 0.0; rows.append(r)  # one zero group
+    rows.append(np.random.default_rng(2).standard_normal(128) * 2.0 ** -100)
+    rows.append(np.random.default_rng(3).standard_normal(128) * 2.0 ** 90)
+    g = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -.5, -1, -1.5, -2, -3, -4, -6, 0.25] * 8)
+    rows.append(g)
+    rows.append(-np.abs(np.random.default_rng(4).standard_normal(128)))
+    e = np.zeros(128); e[5] = 1.0; rows.append(e)
+    e = np.zeros(128); e[100] = -3.0; e[3] = 1e-30; rows.append(e)
+    return bf16_rows(np.array(rows))
+
+
+@pytest.mark.parametrize("nrows", [1, 15, 16, 1000, 4133])
+def test_quantize_bit_exact(fx, nrows):
+    s = synth.signs(300 + nrows)
+    x = synth.normal_bf16(300 + nrows, 3, 0, 0, nrows * 128).reshape(nrows, 128)
+    x = np.concatenate([special_rows(), x])
+    codes, scales = fx.idx_quantize_q(to_dev_bf16(x), torch.from_numpy(s).cuda())
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize(x, s)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def run_full_scan(fx, pl, wl, want_dots=True):
+    dev = pl.DeviceWorkload.from_workload(wl)
+    nq, max_n = dev.nq, dev.max_n
+    qc, qs = fx.idx_quantize_q(dev.q[0], dev.signs)
+    scores = torch.full((nq, max_n), float("nan"), device="cuda")
+    nb = (max_n + 7) // 8
+    bm = torch.full((nq, nb), float("nan"), device="cuda")
+    dots = torch.full((nq, 32, max_n), float("nan"), device="cuda") if want_dots else None
+    fx.idx_score_full(dev.k_codes, dev.k_scales, dev.k_base, dev.n_vis, qc, qs, dev.w[0], max_n, scores=scores,
+                      block_max=bm, head_dots=dots)
+    torch.cuda.synchronize()
+    return dev, scores.cpu().numpy(), bm.cpu().numpy(), (dots.cpu().numpy() if want_dots else None)
+
+
+def test_score_full_parity(fx, pl):
+    wl = synth.decode_workload("p", 201, [1000, 4099, 77, 1, 1024, 0])
+    dev, sc, bm, dots = run_full_scan(fx, pl, wl)
+    s = wl.signs()
+    for t in range(wl.nq):
+        n = int(wl.n_vis[t])
+        if n == 0:
+            assert np.isnan(sc[t]).all() and np.isnan(bm[t]).all()
+            continue
+        kc, ks = oracle.quantize(wl.keys(t), s)
+        qc, qs = oracle.quantize(wl.q(0, [t])[0], s)
+        I, A, D = oracle.score_rows(qc, qs, wl.w(0, [t])[0], kc, ks, want_dots=True)
+        for j in range(32):
+            for e in range(0, n, 97):
+                _, exact, _ = oracle.head_dot(qc[j], qs[j], kc[e], ks[e])
+                assert exact
+        assert np.array_equal(dots[t, :, :n].astype(np.float64), D), f"query {t}: per-head dots differ"
+        assert_scores_close(sc[t, :n], I, A, f"query {t}")
+        assert np.isnan(sc[t, n:]).all(), "scores written past n"
+        nb = (n + 7) // 8
+        ref_bm = oracle.block_max(I, 8)
+        Ab = block_A(A, n)
+        assert np.all(np.abs(bm[t, :nb] - ref_bm) <= TOL * np.maximum(Ab, 1e-30))
+        assert np.isnan(bm[t, nb:]).all(), "block maxima written past ceil(n/8)"
+        # the block maxima are exactly the maxima of the GPU's own scores
+        pad = np.full(nb * 8, -np.inf, np.float32)
+        pad[:n] = sc[t, :n]
+        assert np.array_equal(bm[t, :nb], pad.reshape(nb, 8).max(axis=1))
+
+
+def make_rows(rng, nq, n, kind):
+    if kind == "normal":
+        return rng.standard_normal((nq, n)).astype(np.float32)
+    if kind == "ties":
+        return rng.integers(-3, 4, (nq, n)).astype(np.float32)
+    if kind == "equal":
+        return np.full((nq, n), 1.5, np.float32)
+    if kind == "neginf":
+        a = rng.standard_normal((nq, n)).astype(np.float32)
+        a[rng.random((nq, n)) < 0.7] = -np.inf
+        return a
+    raise KeyError(kind)
+
+
+@pytest.mark.parametrize("n,k,kind", [(1000, 512, "normal"), (70000, 512, "normal"), (5000, 2048, "ties"),
+                                      (3000, 7, "ties"), (20000, 512, "equal"), (9000, 2048, "neginf"),
+                                      (300, 512, "normal"), (1 << 20, 512, "normal"), (1, 1, "normal")])
+def test_topk_exact(fx, n, k, kind):
+    rng = np.random.default_rng(n + k)
+    nq = 3
+    vals = make_rows(rng, nq, n, kind)
+    nvalid = np.array([n, max(n // 2, 0), max(n - 1, 0)], dtype=np.int32)
+    ws = fx.workspace(fx.IDX_OP_TOPK, nq, n, k)
+    out = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
+    oval = torch.empty((nq, k), dtype=torch.float32, device="cuda")
+    fx.idx_topk(torch.from_numpy(vals).cuda(), n, k, out, ws, n_valid=torch.from_numpy(nvalid).cuda(), out_val=oval)
+    torch.cuda.synchronize()
+    out, oval = out.cpu().numpy(), oval.cpu().numpy()
+    for t in range(nq):
+        ref = oracle.topk(vals[t, :nvalid[t]].astype(np.float64), k)
+        assert np.array_equal(out[t], ref), f"row {t}"
+        cnt = int((ref >= 0).sum())
+        assert np.array_equal(oval[t, :cnt], vals[t, ref[:cnt]])
+        assert np.all(np.isneginf(oval[t, cnt:]))
+
+
+@pytest.mark.parametrize("n", [1, 8, 9, 16383, 16384, 16385, 16392, 100003, 1 << 20])
+def test_build_pool_exact(fx, n):
+    rng = np.random.default_rng(n)
+    nq = 2
+    nb = (n + 7) // 8
+    bm = rng.standard_normal((nq, nb)).astype(np.float32)
+    bm[1] = np.round(bm[1])  # ties
+    nv = np.array([n, n], np.int32)
+    ws = fx.workspace(fx.IDX_OP_BUILD_POOL, nq, n, 2048)
+    pb = torch.full((nq, 2048), -7, dtype=torch.int32, device="cuda")
+    pc = torch.empty(nq, dtype=torch.int32, device="cuda")
+    fx.idx_build_pool(torch.from_numpy(bm).cuda(), torch.from_numpy(nv).cuda(), n, pb, pc, ws)
+    torch.cuda.synchronize()
+    pb, pc = pb.cpu().numpy(), pc.cpu().numpy()
+    for t in range(nq):
+        ref = oracle.pool(bm[t].astype(np.float64), n, 8, 2048)
+        assert pc[t] == len(ref)
+        assert np.array_equal(pb[t, :len(ref)], ref)
+        assert (pb[t, len(ref):] == -1).all()
+
+
+def test_gather_matches_full_scan(fx, pl):
+    wl = synth.decode_workload("g", 202, [30000, 3001])
+    dev, sc, bm, _ = run_full_scan(fx, pl, wl, want_dots=False)
+    plan = pl.DecodePlan(dev)
+    plan.q_codes[0], plan.q_scales[0] = fx.idx_quantize_q(dev.q[0], dev.signs)
+    plan.block_max.copy_(torch.from_numpy(bm))
+    plan.build_pool()
+    plan.pool_select(0)
+    torch.cuda.synchronize()
+    pbk = plan.pool_blocks.cpu().numpy()
+    pcn = plan.pool_count.cpu().numpy()
+    ps = plan.pool_scores[0].cpu().numpy()
+    for t in range(wl.nq):
+        n = int(wl.n_vis[t])
+        for i in range(plan.max_blocks):
+            for r in range(8):
+                slot = 8 * i + r
+                if i < pcn[t] and 8 * pbk[t, i] + r < n:
+                    assert ps[t, slot] == sc[t, 8 * pbk[t, i] + r]  # bit-identical arithmetic
+                else:
+                    assert np.isneginf(ps[t, slot])
+
+
+def check_decode(fx, pl, wl, k=512):
+    dev = pl.DeviceWorkload.from_workload(wl)
+    out = pl.decode_step(dev, k=k)
+    torch.cuda.synchronize()
+    s = wl.signs()
+    top = out["topk"].cpu().numpy()
+    pbk, pcn = out["pool_blocks"].cpu().numpy(), out["pool_count"].cpu().numpy()
+    rtop = [r.cpu().numpy() for r in out["reindex_topk"]]
+    for t in range(wl.nq):
+        n = int(wl.n_vis[t])
+        kc, ks = oracle.quantize(wl.keys(t), s)
+        qc, qs = oracle.quantize(wl.q(0, [t])[0], s)
+        I, A = oracle.score_rows(qc, qs, wl.w(0, [t])[0], kc, ks)
+        assert_topk_set(top[t], I, A, k, f"full top-k q{t}")
+        bm = oracle.block_max(I, 8)
+        gpool = pbk[t, :pcn[t]]
+        assert_pool_set(gpool, bm, block_A(A, n), n, 2048, f"pool q{t}")
+        pos = set()
+        for b in gpool:
+            pos.update(range(8 * b, min(8 * b + 8, n)))
+        assert set(int(x) for x in top[t] if x >= 0) <= pos, "Full top-k must lie in the pool"
+        for li in range(wl.layers):
+            qc2, qs2 = oracle.quantize(wl.q(li + 1, [t])[0], s)
+            I2, A2 = oracle.score_rows(qc2, qs2, wl.w(li + 1, [t])[0], kc, ks)
+            # Reindex in the GPU's own pool (mask form); the pool itself is checked above
+            masked = np.full(n, -np.inf)
+            idx = np.array(sorted(pos), dtype=np.int64)
+            masked[idx] = I2[idx]
+            assert_topk_set(rtop[li][t], masked, A2, k, f"reindex layer {li + 1} q{t}")
+            assert set(int(x) for x in rtop[li][t] if x >= 0) <= pos
+
+
+def test_decode_32k_full_size(fx, pl):
+    check_decode(fx, pl, synth.config("decode_32k"))
+
+
+def test_decode_ragged_batch(fx, pl):
+    check_decode(fx, pl, synth.decode_workload("r", 203, [20001, 5000, 700, 16384, 16385, 9], layers=2))
+
+
+def test_prefill_parity(fx, pl):
+    wl = synth.prefill_workload("pf", 204, 6000, 48)
+    dev = pl.DeviceWorkload.from_workload(wl, group=48)
+    plan = pl.PrefillPlan(dev).run()
+    torch.cuda.synchronize()
+    top = plan.topk.cpu().numpy()
+    s = wl.signs()
+    kc, ks = oracle.quantize(wl.keys(0), s)
+    for t in range(0, wl.nq, 5):
+        n = int(wl.n_vis[t])
+        qc, qs = oracle.quantize(wl.q(0, [t])[0], s)
+        I, A = oracle.score_rows(qc, qs, wl.w(0, [t])[0], kc[:n], ks[:n])
+        assert_topk_set(top[t], I, A, 512, f"prefill q{t}")

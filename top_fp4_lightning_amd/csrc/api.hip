@@ -1,0 +1,202 @@
+// C-ABI entry points of libfp4idx: host-side validation, then asynchronous launches.
+// Every check runs before the first HIP call, so argument errors never touch the device.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string>
+
+#include "../../include/fp4idx.h"
+#include "internal.h"
+
+using namespace fp4idx;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+idx_status fail(idx_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+idx_status ok() {
+    g_last_error.clear();
+    return IDX_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+idx_status hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(IDX_EHIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+#define REQUIRE(cond, st, ...)                   \
+    do {                                          \
+        if (!(cond)) return fail(st, __VA_ARGS__); \
+    } while (0)
+
+constexpr int64_t kMaxRows = (int64_t)1 << 36;
+constexpr int64_t kMaxN = (int64_t)1 << 30;
+constexpr int32_t kMaxQueries = 65535;  // grid y dimension
+
+size_t ws_bytes_for(int32_t op, int32_t nq, int64_t max_n, int32_t k) {
+    if (nq < 0 || max_n < 0 || max_n > kMaxN || k < 1 || k > kMaxK) return 0;
+    if (op == IDX_OP_BUILD_POOL) return select_workspace_bytes(nq, (max_n + kBlock - 1) / kBlock, k);
+    if (op == IDX_OP_TOPK) return select_workspace_bytes(nq, max_n, k);
+    return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t idx_abi_version(void) { return IDX_ABI_VERSION; }
+
+const char* idx_last_error(void) { return g_last_error.c_str(); }
+
+size_t idx_workspace_size(int32_t op, int32_t nq, int64_t max_n, int32_t k) {
+    return ws_bytes_for(op, nq, max_n, k);
+}
+
+idx_status idx_quantize_q(const uint16_t* x_bf16, int64_t rows, const int8_t* signs, uint8_t* codes,
+                          uint8_t* scales, void* stream) {
+    REQUIRE(rows >= 0 && rows <= kMaxRows, IDX_EINVAL, "idx_quantize_q: rows=%lld out of [0, 2^36]", (long long)rows);
+    if (rows == 0) return ok();
+    REQUIRE(x_bf16 && signs && codes && scales, IDX_EINVAL, "idx_quantize_q: null pointer");
+    REQUIRE(aligned(x_bf16, 16) && aligned(codes, 16) && aligned(signs, 16) && aligned(scales, 4), IDX_EALIGN,
+            "idx_quantize_q: x, codes and signs must be 16-byte aligned, scales 4-byte aligned");
+    return hip_status(launch_quantize(x_bf16, rows, signs, codes, scales, (hipStream_t)stream), "idx_quantize_q");
+}
+
+idx_status idx_score_full(const uint8_t* k_codes, const uint8_t* k_scales, const int64_t* k_base,
+                          const int32_t* n_vis, int32_t nq, int32_t group, int64_t max_n, const uint8_t* q_codes,
+                          const uint8_t* q_scales, const float* w, float* scores, int64_t score_stride,
+                          float* block_max, int64_t bm_stride, float* head_dots, void* stream) {
+    REQUIRE(nq >= 0 && nq <= kMaxQueries, IDX_EUNSUPPORTED, "idx_score_full: nq=%d out of [0, 65535]", nq);
+    REQUIRE(max_n >= 0 && max_n <= kMaxN, IDX_EINVAL, "idx_score_full: max_n=%lld out of [0, 2^30]",
+            (long long)max_n);
+    REQUIRE(group >= 1 && (nq == 0 || nq % group == 0), IDX_EINVAL, "idx_score_full: group=%d must divide nq=%d",
+            group, nq);
+    REQUIRE(scores || block_max || head_dots, IDX_EINVAL, "idx_score_full: no output requested");
+    if (nq == 0 || max_n == 0) return ok();
+    REQUIRE(k_codes && k_scales && k_base && n_vis && q_codes && q_scales && w, IDX_EINVAL,
+            "idx_score_full: null input pointer");
+    REQUIRE(aligned(k_codes, 16) && aligned(q_codes, 16) && aligned(k_scales, 4) && aligned(q_scales, 4) &&
+                aligned(w, 4) && aligned(k_base, 8) && aligned(n_vis, 4),
+            IDX_EALIGN, "idx_score_full: misaligned input pointer");
+    if (scores || head_dots)
+        REQUIRE(score_stride >= max_n, IDX_EINVAL, "idx_score_full: score_stride=%lld < max_n=%lld",
+                (long long)score_stride, (long long)max_n);
+    if (block_max)
+        REQUIRE(bm_stride >= (max_n + kBlock - 1) / kBlock, IDX_EINVAL,
+                "idx_score_full: bm_stride=%lld < ceil(max_n/8)", (long long)bm_stride);
+    REQUIRE((!scores || aligned(scores, 4)) && (!block_max || aligned(block_max, 4)) &&
+                (!head_dots || aligned(head_dots, 4)),
+            IDX_EALIGN, "idx_score_full: misaligned output pointer");
+    ScoreArgs a{k_codes, k_scales, k_base, n_vis, nq, group, max_n, q_codes, q_scales, w,
+                scores, score_stride, block_max, bm_stride, head_dots};
+    return hip_status(launch_score_full(a, (hipStream_t)stream), "idx_score_full");
+}
+
+idx_status idx_build_pool(const float* block_max, int64_t bm_stride, const int32_t* n_vis, int32_t nq,
+                          int64_t max_n, int32_t topk_blocks, int32_t block, int32_t* pool_blocks,
+                          int64_t pool_stride, int32_t* pool_count, void* ws, size_t ws_bytes, void* stream) {
+    REQUIRE(block == kBlock, IDX_EUNSUPPORTED, "idx_build_pool: block=%d (only 8 is implemented)", block);
+    REQUIRE(topk_blocks >= 1 && topk_blocks <= kMaxK, IDX_EUNSUPPORTED, "idx_build_pool: topk_blocks=%d out of [1, 2048]",
+            topk_blocks);
+    REQUIRE(nq >= 0 && nq <= kMaxQueries, IDX_EUNSUPPORTED, "idx_build_pool: nq=%d out of [0, 65535]", nq);
+    REQUIRE(max_n >= 0 && max_n <= kMaxN, IDX_EINVAL, "idx_build_pool: max_n=%lld out of [0, 2^30]",
+            (long long)max_n);
+    if (nq == 0) return ok();
+    REQUIRE(block_max && n_vis && pool_blocks && pool_count, IDX_EINVAL, "idx_build_pool: null pointer");
+    REQUIRE(bm_stride >= (max_n + kBlock - 1) / kBlock, IDX_EINVAL, "idx_build_pool: bm_stride < ceil(max_n/8)");
+    REQUIRE(pool_stride >= topk_blocks, IDX_EINVAL, "idx_build_pool: pool_stride=%lld < topk_blocks=%d",
+            (long long)pool_stride, topk_blocks);
+    const size_t need = ws_bytes_for(IDX_OP_BUILD_POOL, nq, max_n, topk_blocks);
+    REQUIRE(ws && ws_bytes >= need, IDX_EWORKSPACE, "idx_build_pool: workspace %zu bytes, need %zu", ws_bytes, need);
+    REQUIRE(aligned(ws, 16) && aligned(block_max, 4) && aligned(n_vis, 4) && aligned(pool_blocks, 4) &&
+                aligned(pool_count, 4),
+            IDX_EALIGN, "idx_build_pool: misaligned pointer");
+    SelectArgs a{};
+    a.vals = block_max;
+    a.stride = bm_stride;
+    a.nv = n_vis;
+    a.nq = nq;
+    a.max_n = max_n;
+    a.k = topk_blocks;
+    a.pool_mode = true;
+    a.out_idx = pool_blocks;
+    a.out_stride = pool_stride;
+    a.out_count = pool_count;
+    a.pad_to = topk_blocks;
+    a.ws = ws;
+    return hip_status(launch_select(a, (hipStream_t)stream), "idx_build_pool");
+}
+
+idx_status idx_score_pool_gather(const uint8_t* k_codes, const uint8_t* k_scales, const int64_t* k_base,
+                                 const int32_t* n_vis, int32_t nq, const int32_t* blocks, int64_t blocks_stride,
+                                 const int32_t* block_count, int32_t max_blocks, int32_t block,
+                                 const uint8_t* q_codes, const uint8_t* q_scales, const float* w, float* scores,
+                                 int64_t score_stride, float* head_dots, void* stream) {
+    REQUIRE(block == kBlock, IDX_EUNSUPPORTED, "idx_score_pool_gather: block=%d (only 8 is implemented)", block);
+    REQUIRE(nq >= 0 && nq <= kMaxQueries, IDX_EUNSUPPORTED, "idx_score_pool_gather: nq=%d out of [0, 65535]", nq);
+    REQUIRE(max_blocks >= 0 && max_blocks <= (1 << 20), IDX_EINVAL,
+            "idx_score_pool_gather: max_blocks=%d out of [0, 2^20]", max_blocks);
+    if (nq == 0 || max_blocks == 0) return ok();
+    REQUIRE(k_codes && k_scales && k_base && n_vis && blocks && block_count && q_codes && q_scales && w && scores,
+            IDX_EINVAL, "idx_score_pool_gather: null pointer");
+    REQUIRE(blocks_stride >= max_blocks, IDX_EINVAL, "idx_score_pool_gather: blocks_stride < max_blocks");
+    REQUIRE(score_stride >= (int64_t)max_blocks * kBlock, IDX_EINVAL,
+            "idx_score_pool_gather: score_stride < 8 * max_blocks");
+    REQUIRE(aligned(k_codes, 16) && aligned(q_codes, 16) && aligned(k_scales, 4) && aligned(q_scales, 4) &&
+                aligned(w, 4) && aligned(k_base, 8) && aligned(n_vis, 4) && aligned(blocks, 4) &&
+                aligned(block_count, 4) && aligned(scores, 4) && (!head_dots || aligned(head_dots, 4)),
+            IDX_EALIGN, "idx_score_pool_gather: misaligned pointer");
+    GatherArgs a{k_codes, k_scales, k_base, n_vis, nq, blocks, blocks_stride, block_count, max_blocks,
+                 q_codes, q_scales, w, scores, score_stride, head_dots};
+    return hip_status(launch_score_gather(a, (hipStream_t)stream), "idx_score_pool_gather");
+}
+
+idx_status idx_topk(const float* scores, int64_t score_stride, const int32_t* n_valid, int32_t nq, int64_t max_n,
+                    int32_t k, const int32_t* blocks, int64_t blocks_stride, int32_t block, int32_t* out_idx,
+                    int64_t out_stride, float* out_val, void* ws, size_t ws_bytes, void* stream) {
+    REQUIRE(k >= 1 && k <= kMaxK, IDX_EUNSUPPORTED, "idx_topk: k=%d out of [1, 2048]", k);
+    REQUIRE(nq >= 0 && nq <= kMaxQueries, IDX_EUNSUPPORTED, "idx_topk: nq=%d out of [0, 65535]", nq);
+    REQUIRE(max_n >= 0 && max_n <= kMaxN, IDX_EINVAL, "idx_topk: max_n=%lld out of [0, 2^30]", (long long)max_n);
+    if (blocks) REQUIRE(block == kBlock, IDX_EUNSUPPORTED, "idx_topk: block=%d (only 8 is implemented)", block);
+    if (nq == 0) return ok();
+    REQUIRE(scores && out_idx, IDX_EINVAL, "idx_topk: null pointer");
+    REQUIRE(score_stride >= max_n, IDX_EINVAL, "idx_topk: score_stride < max_n");
+    REQUIRE(out_stride >= k, IDX_EINVAL, "idx_topk: out_stride < k");
+    if (blocks)
+        REQUIRE(blocks_stride >= (max_n + kBlock - 1) / kBlock, IDX_EINVAL, "idx_topk: blocks_stride < ceil(max_n/8)");
+    const size_t need = ws_bytes_for(IDX_OP_TOPK, nq, max_n, k);
+    REQUIRE(ws && ws_bytes >= need, IDX_EWORKSPACE, "idx_topk: workspace %zu bytes, need %zu", ws_bytes, need);
+    REQUIRE(aligned(ws, 16) && aligned(scores, 4) && aligned(out_idx, 4) && (!out_val || aligned(out_val, 4)) &&
+                (!n_valid || aligned(n_valid, 4)) && (!blocks || aligned(blocks, 4)),
+            IDX_EALIGN, "idx_topk: misaligned pointer");
+    SelectArgs a{};
+    a.vals = scores;
+    a.stride = score_stride;
+    a.nv = n_valid;
+    a.nq = nq;
+    a.max_n = max_n;
+    a.k = k;
+    a.pool_mode = false;
+    a.map = blocks;
+    a.map_stride = blocks_stride;
+    a.out_idx = out_idx;
+    a.out_stride = out_stride;
+    a.out_val = out_val;
+    a.out_count = nullptr;
+    a.pad_to = k;
+    a.ws = ws;
+    return hip_status(launch_select(a, (hipStream_t)stream), "idx_topk");
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// Random-Hadamard rotation + MXFP4 quantisation of 128-dim rows (indexer queries and keys).
+//
+// Rotation: sign flip, then the Sylvester Walsh-Hadamard transform computed as a fast transform
+// in fp64 (every partial sum of bf16 inputs is exact), then fl32(S) * fl32(2^-3.5) in fp32.
+// Scale: smallest e with 6 * 2^e >= group max (the ideal max/6 rounded up to a power of two).
+// Codes: E2M1 by threshold comparison on y / 2^e (nearest, ties to the even mantissa bit).
+// Layout: 16 lanes per row, lane i owns elements 8i .. 8i+7; 16 rows per 256-thread block.
+#include "internal.h"
+
+namespace fp4idx {
+namespace {
+
+__device__ __forceinline__ double shfl_xor16(double v, int m) { return __shfl_xor(v, m, 16); }
+__device__ __forceinline__ float shfl_xor16f(float v, int m) { return __shfl_xor(v, m, 16); }
+
+// E2M1 code (0..7) of a magnitude v in [0, 6]: nearest grid value, ties to even mantissa
+__device__ __forceinline__ uint32_t e2m1_mag_code(double a) {
+    uint32_t c;
+    if (a <= 0.25) c = 0;
+    else if (a < 0.75) c = 1;
+    else if (a <= 1.25) c = 2;
+    else if (a < 1.75) c = 3;
+    else if (a <= 2.5) c = 4;
+    else if (a < 3.5) c = 5;
+    else if (a <= 5.0) c = 6;
+    else c = 7;
+    return c;
+}
+
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                       const int8_t* __restrict__ signs, uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
+    const int li = threadIdx.x & 15;
+    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const bool live = row < rows;  // dead lanes still join the shuffles of their 16-lane group
+
+    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+    if (live) raw = *reinterpret_cast<const uint4*>(x + row * kDim + li * 8);
+    const uint2 sg = *reinterpret_cast<const uint2*>(signs + li * 8);
+    const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
+    const uint32_t sw[2] = {sg.x, sg.y};
+
+    double v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t h = (i & 1) ? (words[i >> 1] >> 16) : (words[i >> 1] & 0xffffu);
+        float f = __uint_as_float(h << 16);
+        int s = (int)(int8_t)((sw[i >> 2] >> (8 * (i & 3))) & 0xffu);
+        v[i] = (double)f * (double)s;
+    }
+    // butterflies over element-index bits 1, 2, 4 (inside the lane)
+#pragma unroll
+    for (int b = 1; b < 8; b <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (!(i & b)) {
+                double p = v[i], q = v[i | b];
+                v[i] = p + q;
+                v[i | b] = p - q;
+            }
+        }
+    }
+    // butterflies over element-index bits 8, 16, 32, 64 (lane bits 1, 2, 4, 8)
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+        const bool upper = (li & m) != 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            double p = shfl_xor16(v[i], m);
+            v[i] = upper ? (p - v[i]) : (v[i] + p);
+        }
+    }
+    const float inv = 0x1.6a09e6p-4f;  // fl32(2^-3.5)
+    float y[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float s32 = (float)v[i];
+        y[i] = s32 * inv;
+        amax = fmaxf(amax, fabsf(y[i]));
+    }
+    // group of 32 = 4 consecutive lanes
+    amax = fmaxf(amax, shfl_xor16f(amax, 1));
+    amax = fmaxf(amax, shfl_xor16f(amax, 2));
+
+    int e = -127;
+    const double ad = (double)amax;
+    if (ad > 0.0) {
+        int E;
+        double m = frexp(ad, &E);  // ad = m * 2^E, 0.5 <= m < 1
+        e = (m <= 0.75) ? E - 3 : E - 2;
+        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    }
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        double vd = ldexp((double)y[i], -e);
+        uint32_t c = e2m1_mag_code(fabs(vd));
+        if (c != 0 && vd < 0.0) c |= 8u;
+        packed |= c << (4 * i);
+    }
+    if (live) {
+        *reinterpret_cast<uint32_t*>(codes + row * kRowBytes + li * 4) = packed;
+        if ((li & 3) == 0) scales[row * kGroups + (li >> 2)] = (uint8_t)(e + 127);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const uint16_t* x, int64_t rows, const int8_t* signs, uint8_t* codes, uint8_t* scales,
+                           hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    const int64_t blocks = (rows + 15) / 16;
+    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, signs, codes, scales);
+    return hipGetLastError();
+}
+
+}  // namespace fp4idx

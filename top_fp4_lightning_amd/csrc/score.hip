@@ -1,0 +1,265 @@
+// Indexer scoring on gfx950: scaled-FP4 MFMA for the per-head dots, fused ReLU-weighted head sum,
+// block-8 maxima.
+//
+// Work unit: one wave scores 64 keys per step as four tiles of 16 keys. For a tile, two
+// V_MFMA_SCALE_F32_16X16X128_F8F6F4 ops (FP4 x FP4, one per half of the 32 heads) contract all
+// 128 dims at once: A = the query (16 heads x 128), B = 16 keys x 128. Operand lane layout
+// (verified on the hardware): lane l holds row/column l % 16 and the 32-element K-block l / 16,
+// i.e. 16 code bytes, plus that block's E8M0 scale byte. So a tile's B operand is the 1 KiB of
+// codes of 16 consecutive keys read with one 128-bit load per lane (fully coalesced), and the
+// query stays in registers for the whole scan. Output: lane l holds key l % 16 for heads
+// 4 * (l / 16) + i (i = 0..3) of each half. Each lane sums ReLU(d) * w over its 8 heads; the
+// four lane rows are then combined for four tiles at once with two permlane32 swaps and one
+// permlane16 swap, which leaves the score of key l of the 64-key step in lane l.
+//
+// The scale-FP4 MFMA returns exact per-head dots whenever the per-block scale exponents of a
+// dot stay within a narrow range (exact sums of FP4 products below 2^24 ulps of the smallest
+// block), which the UE8M0 encoding of real activations satisfies; the head sum is fp32.
+#include "internal.h"
+
+namespace fp4idx {
+namespace {
+
+struct QRegs {
+    v8i a[2];     // heads 0-15 and 16-31: this lane's 32-element block of head (l % 16) + 16h
+    int sc[2];    // its UE8M0 scale byte
+    float w[2][4];  // weights of output heads 16h + 4 * (l / 16) + i
+};
+
+__device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales,
+                                           const float* __restrict__ w, int64_t t, int lane, QRegs& q) {
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int head = 16 * h + r;
+        const uint4 c = *reinterpret_cast<const uint4*>(q_codes + ((t * kHeads + head) * kRowBytes + g * 16));
+        q.a[h] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+        q.sc[h] = (int)q_scales[(t * kHeads + head) * kGroups + g];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q.w[h][i] = w[t * kHeads + 16 * h + 4 * g + i];
+    }
+}
+
+// B operand of one tile: key rows given per lane (row < 0: absent key, zero contribution)
+struct KTile {
+    v8i b;
+    int sc;
+};
+
+__device__ __forceinline__ void load_key(const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
+                                         int64_t row, int g, KTile& kt) {
+    if (row >= 0) {
+        const uint4 c = *reinterpret_cast<const uint4*>(k_codes + row * kRowBytes + g * 16);
+        kt.b = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+        kt.sc = (int)k_scales[row * kGroups + g];
+    } else {
+        kt.b = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        kt.sc = 0;
+    }
+}
+
+struct TileOut {
+    v4f d[2];
+};
+
+__device__ __forceinline__ void mfma_tile(const QRegs& q, const KTile& kt, TileOut& o) {
+    const v4f z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        o.d[h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a[h], kt.b, z, 4, 4, 0, q.sc[h], 0, kt.sc);
+}
+
+// this lane's partial score: sum over its 8 heads of w * ReLU(d), fixed order
+__device__ __forceinline__ float lane_partial(const QRegs& q, const TileOut& o) {
+    float p = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p = fmaf(q.w[h][i], fmaxf(o.d[h][i], 0.0f), p);
+    return p;
+}
+
+// combine the four 16-lane rows for four tiles: returns in lane l the score of key l of the step
+__device__ __forceinline__ float combine4(float p0, float p1, float p2, float p3) {
+    // permlane32_swap(x, y): x' = [x.lo, y.lo], y' = [x.hi, y.hi] (32-lane halves)
+    auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
+    auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
+    const float u = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);  // lanes 0-31: tile 0, 32-63: tile 2
+    const float v = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);  // lanes 0-31: tile 1, 32-63: tile 3
+    // permlane16_swap(x, y): x' = [x.r0, y.r0, x.r2, y.r2], y' = [x.r1, y.r1, x.r3, y.r3]
+    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(u), __float_as_uint(v), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+__device__ __forceinline__ float max8(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    return v;
+}
+
+// --------------------------------------------------------------------------------------------
+// Full-layer scan, one query per key range. Grid: x = chunks of 4 waves x ITERS x 64 keys,
+// y = queries. Keys past n_t are neither read nor scored.
+template <int ITERS>
+__global__ __launch_bounds__(256) void score_full_kernel(ScoreArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t t = blockIdx.y;
+    int64_t n = a.n_vis[t];
+    n = n < 0 ? 0 : (n > a.max_n ? a.max_n : n);
+    const int64_t e_begin = ((int64_t)blockIdx.x * 4 + wave) * (ITERS * 64);
+    if (e_begin >= n) return;
+
+    QRegs q;
+    load_query(a.q_codes, a.q_scales, a.w, t, lane, q);
+    const int64_t base = a.k_base[t];
+    const int g = lane >> 4, r = lane & 15;
+
+    KTile cur[4], nxt[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t e = e_begin + 16 * u + r;
+        load_key(a.k_codes, a.k_scales, e < n ? base + e : -1, g, cur[u]);
+    }
+    for (int it = 0; it < ITERS; ++it) {
+        const int64_t e0 = e_begin + (int64_t)it * 64;
+        if (e0 >= n) break;
+        const int64_t e1 = e0 + 64;
+        if (it + 1 < ITERS && e1 < n) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t e = e1 + 16 * u + r;
+                load_key(a.k_codes, a.k_scales, e < n ? base + e : -1, g, nxt[u]);
+            }
+        }
+        float p[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            TileOut o;
+            mfma_tile(q, cur[u], o);
+            p[u] = lane_partial(q, o);
+            if (a.head_dots) {
+                const int64_t e = e0 + 16 * u + r;
+                if (e < n) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            a.head_dots[(t * kHeads + 16 * h + 4 * g + i) * a.score_stride + e] = o.d[h][i];
+                }
+            }
+        }
+        float s = combine4(p[0], p[1], p[2], p[3]);
+        const int64_t e = e0 + lane;
+        const bool valid = e < n;
+        if (a.scores && valid) a.scores[t * a.score_stride + e] = s;
+        if (a.block_max) {
+            const float m = max8(valid ? s : -INFINITY);
+            const int64_t b = e >> 3;
+            if ((lane & 7) == 0 && e < n) a.block_max[t * a.bm_stride + b] = m;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+    }
+}
+
+// --------------------------------------------------------------------------------------------
+// Pool gather: slot 8i + r of query t is position 8 * blocks[t][i] + r. Every slot in
+// [0, 8 * max_blocks) is written (-inf when absent). Grid: x = chunks of slots, y = queries.
+template <int ITERS>
+__global__ __launch_bounds__(256) void score_gather_kernel(GatherArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t t = blockIdx.y;
+    const int64_t slots = (int64_t)a.max_blocks * kBlock;
+    const int64_t s_begin = ((int64_t)blockIdx.x * 4 + wave) * (ITERS * 64);
+    if (s_begin >= slots) return;
+    int64_t cnt = a.block_count[t];
+    cnt = cnt < 0 ? 0 : (cnt > a.max_blocks ? a.max_blocks : cnt);
+    int64_t n = a.n_vis[t];
+    n = n < 0 ? 0 : n;
+
+    QRegs q;
+    load_query(a.q_codes, a.q_scales, a.w, t, lane, q);
+    const int64_t base = a.k_base[t];
+    const int g = lane >> 4, r = lane & 15;
+    const int32_t* blk = a.blocks + t * a.blocks_stride;
+
+    // position of slot s, or -1 if absent
+    auto pos_of = [&](int64_t s) -> int64_t {
+        if (s >= slots) return -1;
+        const int64_t i = s >> 3;
+        if (i >= cnt) return -1;
+        const int64_t b = blk[i];
+        if (b < 0) return -1;
+        const int64_t pos = b * kBlock + (s & 7);
+        return pos < n ? pos : -1;
+    };
+
+    KTile cur[4], nxt[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t pos = pos_of(s_begin + 16 * u + r);
+        load_key(a.k_codes, a.k_scales, pos >= 0 ? base + pos : -1, g, cur[u]);
+    }
+    for (int it = 0; it < ITERS; ++it) {
+        const int64_t s0 = s_begin + (int64_t)it * 64;
+        if (s0 >= slots) break;
+        const int64_t s1 = s0 + 64;
+        if (it + 1 < ITERS && s1 < slots) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t pos = pos_of(s1 + 16 * u + r);
+                load_key(a.k_codes, a.k_scales, pos >= 0 ? base + pos : -1, g, nxt[u]);
+            }
+        }
+        float p[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            TileOut o;
+            mfma_tile(q, cur[u], o);
+            p[u] = lane_partial(q, o);
+            if (a.head_dots) {
+                const int64_t s = s0 + 16 * u + r;
+                if (pos_of(s) >= 0) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            a.head_dots[(t * kHeads + 16 * h + 4 * g + i) * a.score_stride + s] = o.d[h][i];
+                }
+            }
+        }
+        const float sc = combine4(p[0], p[1], p[2], p[3]);
+        const int64_t s = s0 + lane;
+        if (s < slots) a.scores[t * a.score_stride + s] = pos_of(s) >= 0 ? sc : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+    }
+}
+
+constexpr int kScanIters = 4;    // 4 waves x 4 steps x 64 keys = 1024 keys per block
+constexpr int kGatherIters = 4;
+
+}  // namespace
+
+hipError_t launch_score_full(const ScoreArgs& a, hipStream_t stream) {
+    if (a.nq <= 0 || a.max_n <= 0) return hipSuccess;
+    const int64_t per_block = 4 * kScanIters * 64;
+    const int64_t gx = (a.max_n + per_block - 1) / per_block;
+    hipLaunchKernelGGL(score_full_kernel<kScanIters>, dim3((unsigned)gx, (unsigned)a.nq), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_score_gather(const GatherArgs& a, hipStream_t stream) {
+    if (a.nq <= 0 || a.max_blocks <= 0) return hipSuccess;
+    const int64_t per_block = 4 * kGatherIters * 64;
+    const int64_t slots = (int64_t)a.max_blocks * kBlock;
+    const int64_t gx = (slots + per_block - 1) / per_block;
+    hipLaunchKernelGGL(score_gather_kernel<kGatherIters>, dim3((unsigned)gx, (unsigned)a.nq), dim3(256), 0, stream,
+                       a);
+    return hipGetLastError();
+}
+
+}  // namespace fp4idx

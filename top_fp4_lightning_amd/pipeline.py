@@ -1,0 +1,172 @@
+"""Composition of the C-ABI calls into the indexer's per-token steps.
+
+Decode (one query per sequence), following the hierarchical indexer of "DeepSeek-V4.1 model
+structure (3)" (blog.javazero.top, section "use shallow-layer scores to limit deep-layer
+scoring"):
+  1. idx_quantize_q         the Full layer's query
+  2. idx_score_full         every visible key -> block-8 maxima (scores are not written)
+  3. idx_build_pool         pin + top-2048 blocks -> candidate pool
+  4. idx_score_pool_gather  the Full layer's own query over the pool, then idx_topk -> top-512.
+     Exact: a top-512 key's block is outranked by at most 511 unpinned blocks, so it is in
+     the pool, and a pooled key's score is computed by the same per-key arithmetic.
+  5. for each Reindex layer: idx_quantize_q, idx_score_pool_gather, idx_topk -> its top-512.
+
+Prefill (a chunk of queries sharing one key range, causal): idx_score_full writes block maxima
+for every query; idx_topk keeps the 512 best blocks per query (a top-512 key's block is among
+them); idx_score_pool_gather re-scores those 4096 keys; idx_topk takes the final 512.
+
+All buffers are allocated once in the plan objects, so a step allocates nothing and can be
+captured in a HIP graph.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import (BLOCK, IDX_OP_BUILD_POOL, IDX_OP_TOPK, idx_build_pool, idx_quantize_q, idx_score_full,
+               idx_score_pool_gather, idx_topk, workspace)
+
+
+@dataclass
+class DeviceWorkload:
+    """Inputs resident in HBM: quantised key cache, raw bf16 queries per layer, fp32 weights."""
+
+    signs: torch.Tensor  # int8 [128]
+    k_codes: torch.Tensor  # u8 [N, 64]
+    k_scales: torch.Tensor  # u8 [N, 4]
+    k_base: torch.Tensor  # int64 [nq]
+    n_vis: torch.Tensor  # int32 [nq]
+    max_n: int
+    group: int
+    q: list  # per layer: bf16 [nq, 32, 128]
+    w: list  # per layer: f32 [nq, 32]
+
+    @property
+    def nq(self) -> int:
+        return int(self.n_vis.shape[0])
+
+    @staticmethod
+    def from_workload(wl, device="cuda", chunk_rows: int = 1 << 20, group: int = 1) -> "DeviceWorkload":
+        """Generate a seeded workload's keys on the host in chunks and quantise them on the GPU."""
+        signs = torch.from_numpy(wl.signs()).to(device)
+        total = wl.total_keys
+        k_codes = torch.empty(total, 64, dtype=torch.uint8, device=device)
+        k_scales = torch.empty(total, 4, dtype=torch.uint8, device=device)
+        base = wl.seq_base
+        for b in range(wl.nseq):
+            n = int(wl.seq_len[b])
+            for s0 in range(0, n, chunk_rows):
+                cnt = min(chunk_rows, n - s0)
+                raw = torch.from_numpy(wl.keys(b, s0, cnt).view(np.int16)).view(torch.bfloat16).to(device)
+                r0 = int(base[b]) + s0
+                idx_quantize_q(raw, signs, k_codes[r0:r0 + cnt], k_scales[r0:r0 + cnt])
+        q = []
+        w = []
+        for layer in range(wl.layers + 1):
+            qh = wl.q(layer)
+            q.append(torch.from_numpy(qh.view(np.int16)).view(torch.bfloat16).to(device).contiguous())
+            w.append(torch.from_numpy(wl.w(layer)).to(device).contiguous())
+        return DeviceWorkload(signs=signs, k_codes=k_codes, k_scales=k_scales,
+                              k_base=torch.from_numpy(wl.k_base).to(device),
+                              n_vis=torch.from_numpy(wl.n_vis.astype(np.int32)).to(device),
+                              max_n=int(wl.n_vis.max()) if wl.nq else 0, group=group, q=q, w=w)
+
+
+class DecodePlan:
+    """Preallocated buffers for one decode step (Full layer + pool + Reindex layers)."""
+
+    def __init__(self, dev: DeviceWorkload, k: int = 512, topk_blocks: int = 2048, want_scores: bool = False):
+        nq, max_n = dev.nq, dev.max_n
+        d = dev.k_codes.device
+        self.dev, self.k, self.topk_blocks = dev, k, topk_blocks
+        self.layers = len(dev.q) - 1
+        nb = (max_n + BLOCK - 1) // BLOCK
+        self.max_blocks = min(topk_blocks, nb)
+        slots = self.max_blocks * BLOCK
+        self.q_codes = [torch.empty(nq, 32, 64, dtype=torch.uint8, device=d) for _ in dev.q]
+        self.q_scales = [torch.empty(nq, 32, 4, dtype=torch.uint8, device=d) for _ in dev.q]
+        self.block_max = torch.empty(nq, max(nb, 1), dtype=torch.float32, device=d)
+        self.scores = torch.empty(nq, max(max_n, 1), dtype=torch.float32, device=d) if want_scores else None
+        self.pool_blocks = torch.empty(nq, topk_blocks, dtype=torch.int32, device=d)
+        self.pool_count = torch.empty(nq, dtype=torch.int32, device=d)
+        self.pool_scores = [torch.empty(nq, max(slots, 1), dtype=torch.float32, device=d) for _ in dev.q]
+        self.topk = [torch.empty(nq, k, dtype=torch.int32, device=d) for _ in dev.q]
+        self.topk_val = [torch.empty(nq, k, dtype=torch.float32, device=d) for _ in dev.q]
+        self.ws_pool = workspace(IDX_OP_BUILD_POOL, nq, max_n, topk_blocks, device=d)
+        self.ws_topk = workspace(IDX_OP_TOPK, nq, max(slots, 1), k, device=d)
+
+    def quantize(self, layer: int, stream=None):
+        idx_quantize_q(self.dev.q[layer], self.dev.signs, self.q_codes[layer], self.q_scales[layer], stream=stream)
+
+    def full_scan(self, stream=None):
+        dv = self.dev
+        idx_score_full(dv.k_codes, dv.k_scales, dv.k_base, dv.n_vis, self.q_codes[0], self.q_scales[0], dv.w[0],
+                       dv.max_n, group=1, scores=self.scores, block_max=self.block_max, stream=stream)
+
+    def build_pool(self, stream=None):
+        idx_build_pool(self.block_max, self.dev.n_vis, self.dev.max_n, self.pool_blocks, self.pool_count,
+                       self.ws_pool, topk_blocks=self.topk_blocks, stream=stream)
+
+    def pool_select(self, layer: int, stream=None):
+        dv = self.dev
+        idx_score_pool_gather(dv.k_codes, dv.k_scales, dv.k_base, dv.n_vis, self.pool_blocks, self.pool_count,
+                              self.max_blocks, self.q_codes[layer], self.q_scales[layer], dv.w[layer],
+                              self.pool_scores[layer], stream=stream)
+        idx_topk(self.pool_scores[layer], self.max_blocks * BLOCK, self.k, self.topk[layer], self.ws_topk,
+                 out_val=self.topk_val[layer], blocks=self.pool_blocks, stream=stream)
+
+    def run(self, stream=None):
+        self.quantize(0, stream)
+        self.full_scan(stream)
+        self.build_pool(stream)
+        self.pool_select(0, stream)
+        for layer in range(1, self.layers + 1):
+            self.quantize(layer, stream)
+            self.pool_select(layer, stream)
+        return self
+
+
+def decode_step(dev: DeviceWorkload, plan: DecodePlan | None = None, **kw) -> dict:
+    plan = plan or DecodePlan(dev, **kw)
+    plan.run()
+    return {"topk": plan.topk[0], "topk_val": plan.topk_val[0], "pool_blocks": plan.pool_blocks,
+            "pool_count": plan.pool_count, "block_max": plan.block_max,
+            "reindex_topk": plan.topk[1:], "plan": plan}
+
+
+class PrefillPlan:
+    """Preallocated buffers for one prefill chunk: many queries sharing one key range."""
+
+    def __init__(self, dev: DeviceWorkload, k: int = 512):
+        nq, max_n = dev.nq, dev.max_n
+        d = dev.k_codes.device
+        self.dev, self.k = dev, k
+        nb = (max_n + BLOCK - 1) // BLOCK
+        self.nb = nb
+        self.q_codes = torch.empty(nq, 32, 64, dtype=torch.uint8, device=d)
+        self.q_scales = torch.empty(nq, 32, 4, dtype=torch.uint8, device=d)
+        self.block_max = torch.empty(nq, max(nb, 1), dtype=torch.float32, device=d)
+        self.n_blocks = ((dev.n_vis.to(torch.int64) + BLOCK - 1) // BLOCK).to(torch.int32)
+        self.kb = min(k, nb)
+        self.top_blocks = torch.empty(nq, k, dtype=torch.int32, device=d)
+        self.block_count = torch.full((nq,), self.kb, dtype=torch.int32, device=d)
+        self.cand_scores = torch.empty(nq, max(self.kb * BLOCK, 1), dtype=torch.float32, device=d)
+        self.topk = torch.empty(nq, k, dtype=torch.int32, device=d)
+        self.topk_val = torch.empty(nq, k, dtype=torch.float32, device=d)
+        self.ws_blocks = workspace(IDX_OP_TOPK, nq, max(nb, 1), k, device=d)
+        self.ws_final = workspace(IDX_OP_TOPK, nq, max(self.kb * BLOCK, 1), k, device=d)
+
+    def run(self, stream=None):
+        dv = self.dev
+        idx_quantize_q(dv.q[0], dv.signs, self.q_codes, self.q_scales, stream=stream)
+        idx_score_full(dv.k_codes, dv.k_scales, dv.k_base, dv.n_vis, self.q_codes, self.q_scales, dv.w[0], dv.max_n,
+                       group=dv.group, block_max=self.block_max, stream=stream)
+        idx_topk(self.block_max, self.nb, self.k, self.top_blocks, self.ws_blocks, n_valid=self.n_blocks,
+                 stream=stream)
+        idx_score_pool_gather(dv.k_codes, dv.k_scales, dv.k_base, dv.n_vis, self.top_blocks, self.block_count,
+                              self.kb, self.q_codes, self.q_scales, dv.w[0], self.cand_scores, stream=stream)
+        idx_topk(self.cand_scores, self.kb * BLOCK, self.k, self.topk, self.ws_final, out_val=self.topk_val,
+                 blocks=self.top_blocks, stream=stream)
+        return self
