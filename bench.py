@@ -1,0 +1,169 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode step of the FP4 lightning indexer at 1M context on one MI355X.
+
+Workload ("fullscan_1m"): 8 sequences x 2^20 visible compressed keys (decoder, m = 1), one
+query each, 32 heads x 128 dims, MXFP4 queries and keys, synthetic seeded inputs. One step is the
+whole hot path for that batch: quantise the Full layer's queries, scan every key (block-8
+maxima fused), build the candidate pool (pin + top-2048 blocks), take the Full layer's top-512,
+then 4 Reindex layers (quantise their queries, gather-score the pool, top-512 each).
+
+Prints one JSON line: entries scored per second over the step (Full-layer keys + pooled keys of
+the Reindex layers), top-512 queries per second, the scan kernel's HBM roofline fraction
+(achieved from HIP events around the scan launches of the timed steps), and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def scan_bytes(n_vis, nq: int) -> int:
+    """algorithmic bytes of one scan launch: 68 B per key, q (32 x 68 B) + w (128 B) per query,
+    4 B per block maximum written"""
+    keys = int(sum(n_vis))
+    blocks = int(sum((n + 7) // 8 for n in n_vis))
+    return keys * 68 + nq * (32 * 68 + 32 * 4) + blocks * 4
+
+
+def cpu_baseline(wl, max_queries: int = 8) -> dict:
+    """The oracle (plain C, threaded over queries) on a bounded sample: the Full layer of the
+    first min(8, cores) sequences of the same workload (score every key, top-512, block maxima,
+    pin, pool). The oracle quantises its own keys first (untimed)."""
+    import numpy as np
+
+    import oracle
+
+    cores = os.cpu_count() or 1
+    nqs = max(1, min(max_queries, wl.nq, cores))
+    s = wl.signs()
+    log(f"cpu baseline: oracle quantises {nqs} x {int(wl.seq_len[0])} keys (untimed)")
+    kcs, kss = [], []
+    for b in range(nqs):
+        kc, ks = oracle.quantize(wl.keys(b), s, nthreads=cores)
+        kcs.append(kc)
+        kss.append(ks)
+    kc = np.concatenate(kcs)
+    ks = np.concatenate(kss)
+    qc, qs = oracle.quantize(wl.q(0, range(nqs)), s)
+    w = wl.w(0, range(nqs))
+    n = wl.n_vis[:nqs].astype(np.int64)
+    base = np.concatenate([[0], np.cumsum(n)[:-1]]).astype(np.int64)
+    log(f"cpu baseline: timing the oracle Full layer on {nqs} queries with {nqs} threads")
+    t0 = time.perf_counter()
+    oracle.decode_batch(kc, ks, base, n, qc, qs, w, k=wl.k, nthreads=nqs)
+    dt = time.perf_counter() - t0
+    entries = int(n.sum())
+    return {"value": entries / dt, "unit": "entries/s", "cores": nqs, "kind": "oracle",
+            "sample": f"Full layer (score all keys, top-512, block max, pin, top-2048 pool) of {nqs} of the "
+                      f"{wl.nq} sequences x {int(n[0])} keys; {dt:.2f} s wall on {nqs} threads",
+            "seconds": round(dt, 3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="fullscan_1m")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the indexer shards by "
+              "sequence with no exchange, or by key range with one all-gather of per-shard candidates)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    import top_fp4_lightning_amd as fx
+    from top_fp4_lightning_amd import pipeline
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = synth.config(args.workload)
+    t = time.perf_counter()
+    dev = pipeline.DeviceWorkload.from_workload(wl)
+    torch.cuda.synchronize()
+    log(f"workload {wl.name}: {wl.nq} queries, {wl.total_keys} keys, {wl.layers} Reindex layers; "
+        f"setup {time.perf_counter() - t:.1f} s")
+    plan = pipeline.DecodePlan(dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        plan.quantize(0)
+        if ev is not None:
+            ev[0].record(stream)
+        plan.full_scan()
+        if ev is not None:
+            ev[1].record(stream)
+        plan.build_pool()
+        plan.pool_select(0)
+        for layer in range(1, plan.layers + 1):
+            plan.quantize(layer)
+            plan.pool_select(layer)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1000.0 / args.steps
+    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    n_vis = [int(x) for x in wl.n_vis]
+    pool_pos = int(sum(min(n, 8 * min(2048, (n + 7) // 8)) for n in n_vis))
+    entries = int(sum(n_vis)) + plan.layers * pool_pos
+    queries = wl.nq * (1 + plan.layers)
+    sb = scan_bytes(n_vis, wl.nq)
+    achieved = sb / (scan_ms / 1000.0) / 1e9
+    res = {
+        "metric": "indexer entries scored/s + top-512 queries/s at 1M ctx; % of HBM roofline",
+        "value": entries / (ms_step / 1000.0),
+        "unit": "entries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic (seeded N(0,1) bf16 q/k, N(0,1/32) w, 1% planted keys; no trained weights)",
+        "config": {"workload": "fullscan_1m decode step: batch 8 x 1048576 keys (m=1), Full scan + top-512 + "
+                               "pool(2048 blocks of 8) + 4 Reindex layers",
+                   "batch": wl.nq, "context": n_vis[0], "reindex_layers": plan.layers, "k": 512,
+                   "pool_blocks": 2048, "block": 8},
+        "top512_queries_per_s": queries / (ms_step / 1000.0),
+        "full_scan_entries_per_s": int(sum(n_vis)) / (scan_ms / 1000.0),
+        "scan_ms": scan_ms,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "score_full_kernel", "algorithmic_bytes_per_launch": sb},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -137,8 +137,11 @@ idx_status idx_score_full(const uint8_t* k_codes, const uint8_t* k_scales, const
  *   pool_stride: >= topk_blocks.
  *   pool_count : device int32 [nq] (written).
  *   ws, ws_bytes : device workspace of at least idx_workspace_size(IDX_OP_BUILD_POOL, nq, max_n,
- *                  topk_blocks) bytes, 16-byte aligned; its contents need no initialisation and
- *                  are clobbered. Calls that run concurrently need separate workspaces.
+ *                  topk_blocks) bytes, 16-byte aligned. It must be zero-filled before its first
+ *                  use (e.g. when allocated); every call restores the counters and histograms it
+ *                  holds to zero before it completes, so the workspace can be reused without
+ *                  clearing (also inside a captured graph). Calls that may run concurrently need
+ *                  separate workspaces.
  */
 idx_status idx_build_pool(const float* block_max, int64_t bm_stride, const int32_t* n_vis, int32_t nq,
                           int64_t max_n, int32_t topk_blocks, int32_t block, int32_t* pool_blocks,
@@ -170,8 +173,12 @@ idx_status idx_score_pool_gather(const uint8_t* k_codes, const uint8_t* k_scales
 
 /*
  * idx_topk: the k largest values of each row ([P1] "use shallow-layer scores...": each layer keeps
- * its own top-512), ranked by (value desc, index asc); -inf (and NaN) values never enter the
- * selection. Output per row: min(k, number of eligible values) indices in rank order, then -1.
+ * its own top-512), ranked by (value desc, index asc) so that ties at the k-th value go to the
+ * lower index; -inf (and NaN) values never enter the selection. Output per row: the
+ * min(k, number of eligible values) selected indices in ascending index order (the order in
+ * which a consumer gathers the selected keys), then -1. With a block map the order is ascending
+ * slot order, which is ascending position when the map is ascending (as idx_build_pool and
+ * idx_topk produce it); rows longer than 16384 values are always reported by ascending position.
  *
  *   scores       : device fp32 [nq][score_stride]; row t uses values 0 .. n_t - 1.
  *   n_valid      : device int32 [nq] or NULL (NULL means max_n for every row);
@@ -184,9 +191,11 @@ idx_status idx_score_pool_gather(const uint8_t* k_codes, const uint8_t* k_scales
  *                  reported index and the tie-break key.
  *   block        : 8 when blocks is given (ignored otherwise).
  *   out_idx      : device int32 [nq][out_stride], out_stride >= k.
- *   out_val      : device fp32 [nq][out_stride] or NULL; -inf after the selected values.
+ *   out_val      : device fp32 [nq][out_stride] or NULL: the selected values in the same order,
+ *                  -inf after them.
  *   ws, ws_bytes : at least idx_workspace_size(IDX_OP_TOPK, nq, max_n, k) bytes, 16-byte aligned,
- *                  clobbered; separate workspaces for concurrent calls.
+ *                  zero-filled before first use; every call restores its counters (as for
+ *                  idx_build_pool); separate workspaces for calls that may run concurrently.
  */
 idx_status idx_topk(const float* scores, int64_t score_stride, const int32_t* n_valid, int32_t nq, int64_t max_n,
                     int32_t k, const int32_t* blocks, int64_t blocks_stride, int32_t block, int32_t* out_idx,

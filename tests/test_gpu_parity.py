@@ -135,9 +135,11 @@ def test_topk_exact(fx, n, k, kind):
     out, oval = out.cpu().numpy(), oval.cpu().numpy()
     for t in range(nq):
         ref = oracle.topk(vals[t, :nvalid[t]].astype(np.float64), k)
-        assert np.array_equal(out[t], ref), f"row {t}"
         cnt = int((ref >= 0).sum())
-        assert np.array_equal(oval[t, :cnt], vals[t, ref[:cnt]])
+        ref_pos = np.sort(ref[:cnt])  # the library reports the selected set in ascending position order
+        assert np.array_equal(out[t, :cnt], ref_pos), f"row {t}"
+        assert (out[t, cnt:] == -1).all()
+        assert np.array_equal(oval[t, :cnt], vals[t, ref_pos])
         assert np.all(np.isneginf(oval[t, cnt:]))
 
 
@@ -152,8 +154,13 @@ def test_build_pool_exact(fx, n):
     ws = fx.workspace(fx.IDX_OP_BUILD_POOL, nq, n, 2048)
     pb = torch.full((nq, 2048), -7, dtype=torch.int32, device="cuda")
     pc = torch.empty(nq, dtype=torch.int32, device="cuda")
-    fx.idx_build_pool(torch.from_numpy(bm).cuda(), torch.from_numpy(nv).cuda(), n, pb, pc, ws)
+    bm_d, nv_d = torch.from_numpy(bm).cuda(), torch.from_numpy(nv).cuda()
+    fx.idx_build_pool(bm_d, nv_d, n, pb, pc, ws)
     torch.cuda.synchronize()
+    pb2 = torch.full((nq, 2048), -7, dtype=torch.int32, device="cuda")
+    fx.idx_build_pool(bm_d, nv_d, n, pb2, pc, ws)  # reuse without clearing
+    torch.cuda.synchronize()
+    assert torch.equal(pb, pb2)
     pb, pc = pb.cpu().numpy(), pc.cpu().numpy()
     for t in range(nq):
         ref = oracle.pool(bm[t].astype(np.float64), n, 8, 2048)
@@ -238,3 +245,27 @@ def test_prefill_parity(fx, pl):
         qc, qs = oracle.quantize(wl.q(0, [t])[0], s)
         I, A = oracle.score_rows(qc, qs, wl.w(0, [t])[0], kc[:n], ks[:n])
         assert_topk_set(top[t], I, A, 512, f"prefill q{t}")
+
+
+@pytest.mark.parametrize("nblocks,k", [(300, 512), (2048, 512), (4096, 2048), (2048, 100)])
+def test_topk_with_block_map(fx, nblocks, k):
+    # slot s stands for position 8 * map[s // 8] + s % 8; ties break on the mapped position
+    rng = np.random.default_rng(nblocks + k)
+    nq = 2
+    slots = nblocks * 8
+    vals = rng.integers(-5, 6, (nq, slots)).astype(np.float32)
+    vals[:, rng.random(slots) < 0.1] = -np.inf
+    maps = np.stack([rng.permutation(50000)[:nblocks] for _ in range(nq)]).astype(np.int32)
+    ws = fx.workspace(fx.IDX_OP_TOPK, nq, slots, k)
+    out = torch.empty((nq, k), dtype=torch.int32, device="cuda")
+    fx.idx_topk(torch.from_numpy(vals).cuda(), slots, k, out, ws, blocks=torch.from_numpy(maps).cuda())
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for t in range(nq):
+        pos = (8 * maps[t][:, None] + np.arange(8)[None, :]).reshape(-1)
+        full = np.full(int(pos.max()) + 1, -np.inf)
+        full[pos] = vals[t]
+        ref = oracle.topk(full, k)
+        cnt = int((ref >= 0).sum())
+        assert sorted(out[t, :cnt].tolist()) == sorted(ref[:cnt].tolist()), f"row {t}"
+        assert (out[t, cnt:] == -1).all()

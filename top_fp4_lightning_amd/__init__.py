@@ -82,10 +82,11 @@ def workspace_size(op: int, nq: int, max_n: int, k: int) -> int:
 
 
 def workspace(op: int, nq: int, max_n: int, k: int, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace; the library restores its counters after every call."""
     n = workspace_size(op, nq, max_n, k)
     if n == 0:
         raise ValueError("invalid workspace request")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def idx_quantize_q(x: torch.Tensor, signs: torch.Tensor, codes: torch.Tensor | None = None,

@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) void score_gather_kernel(GatherArgs a) {
 }
 
 constexpr int kScanIters = 4;    // 4 waves x 4 steps x 64 keys = 1024 keys per block
-constexpr int kGatherIters = 4;
+constexpr int kGatherIters = 1;
 
 }  // namespace
 

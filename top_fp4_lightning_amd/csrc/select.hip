@@ -1,33 +1,45 @@
 // Exact top-k selection (k <= 2048) over rows of fp32 values, ranked by (value desc, index asc).
 //
-// Keys: the fp32 bit pattern mapped to an order-preserving uint32; a 64-bit composite
-// (key << 32) | ~index is unique per element and orders exactly like (value desc, index asc).
-// -inf and NaN are not eligible.
+// Every element gets a unique 64-bit composite c = (key << 32) | ~pos, where key is the fp32
+// bit pattern mapped to an order-preserving uint32 and pos the element's reported index; -inf
+// and NaN get c = 0 (never selected). The top k are exactly the elements with c >= T, where T
+// is found by radix passes of 11 bits over the composite (most significant digit first): each
+// pass histograms the digit among elements matching the digits fixed so far, takes the digit
+// where the count from the top reaches the number still needed, and stops as soon as every
+// element on that digit is needed. Histograms are private per wavefront (two 16-bit counters per
+// LDS word); the summed histogram is stored with one pad word per 32 bins so that a lane can
+// read its own 32 consecutive bins without bank conflicts.
 //
-//  1. clear   : zero the per-row histograms and counters in the workspace.
-//  2. hist    : histogram of the top 11 key bits per row (LDS, then global atomics).
-//  3. filter  : each block recomputes the threshold digit from the row histogram; elements above
-//               it are certainly selected ("sure"), elements on it are candidates. Appends use
-//               one atomic per wavefront (ballot + popcount).
-//  4. finish  : one block per row runs radix passes over the candidates' remaining 53 composite
-//               bits until exactly k are chosen, then bitonic-sorts the k composites in LDS and
-//               writes indices (and values).
-// Pool mode (candidate pool of the hierarchical indexer): values are block maxima, the block of
-// position n-1 is pinned to +inf, and the kept block ids are written in ascending order.
+// The winners are written in ascending position order (the natural order for gathering the
+// selected keys afterwards), with no sort on the hot paths:
+//  - rows of at most 16384 values: one 1024-thread block per row, 16 composites per thread in
+//    registers (one launch); winners are compacted in slot order with wavefront ballots, which is
+//    position order when the optional block map is ascending (as the pool and this function
+//    produce);
+//  - longer rows (candidate pool over 2^17 block maxima, full score rows): three launches over
+//    chunks of 4096 values, ordered by kernel boundaries (no cross-block fences):
+//      hist   - chunk histogram of the top 11 key bits, added to the row histogram (atomics);
+//      filter - every chunk derives the threshold digit from the row histogram; values above it
+//               are certain winners, values on it candidates; both are appended to workspace
+//               lists (one reservation atomic per chunk and list);
+//      finish - one block per row finishes the radix passes over the candidates, orders the
+//               winners (LDS bitmap for pool block ids, else a bitonic sort by position), writes
+//               them and clears the row's histogram and counters for the next call.
 #include "internal.h"
 
 namespace fp4idx {
 namespace {
 
-struct RowCtl {
-    uint32_t sure;
-    uint32_t cand;
-    int32_t thr_bin;
-    uint32_t total;
-};
-
-constexpr int kChunk = 4096;  // elements per block in hist / filter
+constexpr int kSmallRow = 16384;
+constexpr int kSmallThreads = 1024;
+constexpr int kPer = 16;  // values per thread
+constexpr int kLargeThreads = 256;
+constexpr int kChunk = kLargeThreads * kPer;
 constexpr int kFinishThreads = 1024;
+constexpr int kPadBins = kHistBins + kHistBins / 32;
+constexpr int64_t kBitmapMax = (int64_t)1 << 18;  // pool rows up to this many blocks use the bitmap
+
+__device__ __forceinline__ int hidx(int b) { return b + (b >> 5); }
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -38,29 +50,16 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 }
 // finite or +inf; excludes -inf (0x007fffff) and NaN (keys above +inf's 0xff800000)
 __device__ __forceinline__ bool eligible(uint32_t k) { return k > 0x007fffffu && k <= 0xff800000u; }
-
-struct WsView {
-    uint32_t* hist;  // [nq][2048]
-    RowCtl* ctl;     // [nq]
-    uint64_t* sel;   // [nq][k]
-    uint64_t* cand;  // [nq][cap]
-    int64_t cap;
-};
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t pos) {
+    return ((uint64_t)key << 32) | (uint64_t)(~pos);
+}
+__device__ __forceinline__ uint32_t comp_pos(uint64_t c) { return ~(uint32_t)c; }
+__device__ __forceinline__ uint32_t comp_key(uint64_t c) { return (uint32_t)(c >> 32); }
 
 __host__ __device__ inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-__host__ __device__ inline WsView ws_view(void* ws, int32_t nq, int64_t cap, int32_t k) {
-    char* p = (char*)ws;
-    WsView v;
-    v.hist = (uint32_t*)p;
-    p += align_up((size_t)nq * kHistBins * 4);
-    v.ctl = (RowCtl*)p;
-    p += align_up((size_t)nq * sizeof(RowCtl));
-    v.sel = (uint64_t*)p;
-    p += align_up((size_t)nq * k * 8);
-    v.cand = (uint64_t*)p;
-    v.cap = cap;
-    return v;
+__host__ __device__ inline int64_t row_cap(const SelectArgs& a) {
+    return a.pool_mode ? (a.max_n + kBlock - 1) / kBlock : a.max_n;
 }
 
 struct RowInfo {
@@ -82,74 +81,382 @@ __device__ __forceinline__ RowInfo row_info(const SelectArgs& a, int64_t t) {
     return ri;
 }
 
-__device__ __forceinline__ uint32_t key_at(const SelectArgs& a, int64_t t, int64_t i, const RowInfo& ri) {
-    if (i == ri.pin) return 0xff800000u;  // +inf
-    return order_key(a.vals[t * a.stride + i]);
+// Composites of elements base + j * stride, j < E (0 if absent or not eligible). All loads are
+// issued before any is used (clamped in-bounds indices, masked afterwards).
+template <int E>
+__device__ __forceinline__ void load_composites(const SelectArgs& a, int64_t t, const RowInfo& ri, int64_t base,
+                                                int64_t stride, uint64_t (&c)[E]) {
+    if (ri.len <= 0) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) c[j] = 0ull;
+        return;
+    }
+    float v[E];
+    int32_t m[E];
+    const float* row = a.vals + t * a.stride;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        const int64_t i = base + j * stride;
+        v[j] = row[i < ri.len ? i : ri.len - 1];
+    }
+    if (a.map) {
+        const int32_t* mrow = a.map + t * a.map_stride;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const int64_t i = base + j * stride;
+            m[j] = mrow[(i < ri.len ? i : ri.len - 1) >> 3];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        const int64_t i = base + j * stride;
+        const uint32_t k = i == ri.pin ? 0xff800000u : order_key(v[j]);  // the pinned block is +inf
+        if (i >= ri.len || !eligible(k)) {
+            c[j] = 0ull;
+        } else {
+            const uint32_t pos = a.map ? (uint32_t)(m[j] * kBlock + (int32_t)(i & 7)) : (uint32_t)i;
+            c[j] = composite(k, pos);
+        }
+    }
 }
 
-__device__ __forceinline__ uint32_t pos_at(const SelectArgs& a, int64_t t, int64_t i) {
-    if (a.map) return (uint32_t)(a.map[t * a.map_stride + (i >> 3)] * kBlock + (int32_t)(i & 7));
-    return (uint32_t)i;
+__device__ __constant__ int kShift[6] = {53, 42, 31, 20, 9, 0};
+__device__ __constant__ int kWidth[6] = {11, 11, 11, 11, 11, 9};
+
+struct Sel {
+    int digit;
+    uint32_t above;
+};
+
+// ---- wave-private histograms: hw[wave][1024] words, two 16-bit bins per word ----
+template <int NT>
+struct Hist {
+    static constexpr int kWaves = NT / 64;
+    uint32_t hw[kWaves][kHistBins / 2];
+    uint32_t h[kPadBins];  // summed histogram, bin b at hidx(b)
+};
+
+template <int NT>
+__device__ __forceinline__ void hist_clear_own(Hist<NT>& H) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < kHistBins / 2 / 64; ++i) H.hw[w][l + 64 * i] = 0u;
 }
 
-__global__ void select_clear_kernel(uint32_t* hist, RowCtl* ctl, int32_t nq) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t nh = (int64_t)nq * kHistBins;
-    if (i < nh) hist[i] = 0u;
-    if (i < nq) ctl[i] = RowCtl{0u, 0u, -1, 0u};
+template <int NT>
+__device__ __forceinline__ void hist_add(Hist<NT>& H, uint32_t digit) {
+    atomicAdd(&H.hw[threadIdx.x >> 6][digit >> 1], 1u << (16 * (digit & 1)));
 }
 
-__global__ __launch_bounds__(256) void select_hist_kernel(SelectArgs a, WsView v) {
-    __shared__ uint32_t h[kHistBins];
+template <int NT>
+__device__ __forceinline__ void hist_reduce(Hist<NT>& H) {
+    for (int b = threadIdx.x; b < kHistBins; b += NT) {
+        uint32_t s = 0;
+#pragma unroll
+        for (int w = 0; w < Hist<NT>::kWaves; ++w) s += (H.hw[w][b >> 1] >> (16 * (b & 1))) & 0xffffu;
+        H.h[hidx(b)] = s;
+    }
+}
+
+// Threshold digit of the padded histogram h: the largest d with sum_{b >= d} h[b] >= need
+// (d = -1 when the total is below need); `above` = count in bins above d. Wave 0 computes;
+// ends with a barrier. Lane l owns bins [32l, 32l + 32).
+__device__ void block_threshold(const uint32_t* h, uint32_t need, Sel& sel) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        uint32_t s = 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) s += h[33 * lane + j];
+        uint32_t suf = s;  // inclusive suffix sum over lanes
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t o = __shfl_down(suf, off);
+            if (lane + off < 64) suf += o;
+        }
+        const uint32_t total = __shfl(suf, 0);
+        if (total < need) {
+            if (lane == 0) {
+                sel.digit = -1;
+                sel.above = total;
+            }
+        } else {
+            const uint64_t own = __ballot(suf - s < need && need <= suf);
+            const int L = __ffsll((unsigned long long)own) - 1;
+            const uint32_t aboveL = __shfl(suf - s, L);
+            const uint32_t v = lane < 32 ? h[33 * L + lane] : 0u;
+            uint32_t vs = v;  // inclusive suffix over lanes 0..31
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) {
+                const uint32_t o = __shfl_down(vs, off);
+                if (lane + off < 32) vs += o;
+            }
+            const bool hit = lane < 32 && aboveL + vs >= need && aboveL + vs - v < need;
+            const uint64_t hm = __ballot(hit);
+            const int J = __ffsll((unsigned long long)hm) - 1;
+            const uint32_t aboveJ = aboveL + __shfl(vs - v, J);
+            if (lane == 0) {
+                sel.digit = 32 * L + J;
+                sel.above = aboveJ;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// One radix pass over the elements delivered by `each` (a callable that invokes its argument
+// on every composite of this thread); returns true and sets T when the selection is complete.
+template <int NT, class Each>
+__device__ bool radix_pass(Each each, int p, uint32_t& need, uint64_t& prefix, uint64_t& mask, uint64_t& T,
+                           Hist<NT>& H, Sel& sel) {
+    const int shf = kShift[p];
+    const uint64_t dm = ((uint64_t)1 << kWidth[p]) - 1;
+    __syncthreads();
+    hist_clear_own(H);
+    each([&](uint64_t c) {
+        if (c != 0 && ((c ^ prefix) & mask) == 0) hist_add(H, (uint32_t)((c >> shf) & dm));
+    });
+    __syncthreads();
+    hist_reduce(H);
+    __syncthreads();
+    block_threshold(H.h, need, sel);
+    const int d = sel.digit;
+    const uint32_t above = sel.above;
+    if (d < 0) {  // fewer than `need` present: take every eligible element
+        T = 1ull;
+        return true;
+    }
+    if (H.h[hidx(d)] == need - above) {
+        T = prefix | ((uint64_t)d << shf);
+        return true;
+    }
+    need -= above;
+    prefix |= (uint64_t)d << shf;
+    mask |= dm << shf;
+    if (p == 5) {
+        T = prefix;
+        return true;
+    }
+    return false;
+}
+
+// exclusive scan of one value per thread over the block (NT threads); returns the prefix,
+// sets *total
+template <int NT>
+__device__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* wsum, uint32_t* total) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t v = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(v, off);
+        if (lane >= off) v += y;
+    }
+    __syncthreads();
+    if (lane == 63) wsum[w] = v;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const uint32_t s = lane < NW ? wsum[lane] : 0u;
+        uint32_t u = s;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(u, off);
+            if (lane >= off) u += y;
+        }
+        if (lane < NW) wsum[lane] = u - s;
+        if (lane == 63) *total = u;
+    }
+    __syncthreads();
+    return wsum[w] + v - x;
+}
+
+__device__ __forceinline__ uint64_t cmpx(uint64_t v, uint64_t p, bool keep_min) {
+    return keep_min ? (v < p ? v : p) : (v < p ? p : v);
+}
+
+// ascending bitonic sort of s[0..N) (N a power of two <= 2048) by NT threads; element i lives in
+// thread i % NT, register slot i / NT.
+template <int NT>
+__device__ void block_sort(uint64_t* s, int N) {
+    constexpr int Q = kMaxK / NT;
+    const int tid = threadIdx.x;
+    uint64_t v[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) v[q] = tid + q * NT < N ? s[tid + q * NT] : 0ull;
+    for (int size = 2; size <= N; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= NT) {
+                const int qs = stride / NT;
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    if (q & qs) continue;
+                    const int i = tid + q * NT;
+                    const bool up = (i & size) == 0;
+                    const uint64_t x = v[q], y = v[q | qs];
+                    v[q] = cmpx(x, y, up);
+                    v[q | qs] = cmpx(x, y, !up);
+                }
+            } else if (stride >= 64) {
+                __syncthreads();
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+                    if (tid + q * NT < N) s[tid + q * NT] = v[q];
+                __syncthreads();
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const int i = tid + q * NT;
+                    if (i < N) {
+                        const int j = i ^ stride;
+                        v[q] = cmpx(v[q], s[j], (i < j) == ((i & size) == 0));
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const int i = tid + q * NT;
+                    const uint64_t p = __shfl_xor(v[q], stride);
+                    const int j = i ^ stride;
+                    if (i < N) v[q] = cmpx(v[q], p, (i < j) == ((i & size) == 0));
+                }
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+        if (tid + q * NT < N) s[tid + q * NT] = v[q];
+    __syncthreads();
+}
+
+__device__ __forceinline__ void write_one(const SelectArgs& a, int64_t t, int slot, uint64_t c) {
+    a.out_idx[t * a.out_stride + slot] = (int32_t)comp_pos(c);
+    if (a.out_val && !a.pool_mode) a.out_val[t * a.out_stride + slot] = key_value(comp_key(c));
+}
+
+__device__ __forceinline__ void write_pad(const SelectArgs& a, int64_t t, uint32_t cnt) {
+    for (int i = (int)cnt + threadIdx.x; i < a.pad_to; i += blockDim.x) {
+        a.out_idx[t * a.out_stride + i] = -1;
+        if (a.out_val && !a.pool_mode) a.out_val[t * a.out_stride + i] = -INFINITY;
+    }
+    if (a.out_count && threadIdx.x == 0) a.out_count[t] = (int32_t)cnt;
+}
+
+// ---------------------------------------------------------------- rows of <= 16384 values
+__global__ __launch_bounds__(kSmallThreads) void select_small_kernel(SelectArgs a) {
+    constexpr int NW = kSmallThreads / 64;
+    __shared__ Hist<kSmallThreads> H;
+    __shared__ Sel sel;
+    __shared__ uint32_t woff[kPer][NW];
+    const int64_t t = blockIdx.x;
+    const RowInfo ri = row_info(a, t);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint64_t c[kPer];
+    load_composites<kPer>(a, t, ri, threadIdx.x, kSmallThreads, c);
+    auto each = [&](auto&& f) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) f(c[j]);
+    };
+    uint32_t need = (uint32_t)a.k;
+    uint64_t prefix = 0ull, mask = 0ull, T = ~0ull;
+    if (ri.len > 0)
+        for (int p = 0; p < 6; ++p)
+            if (radix_pass<kSmallThreads>(each, p, need, prefix, mask, T, H, sel)) break;
+    // ordered compaction: slot order (j, wave, lane)
+    uint64_t m[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        m[j] = __ballot(c[j] != 0 && c[j] >= T);
+        if (lane == 0) woff[j][w] = (uint32_t)__popcll(m[j]);
+    }
+    __syncthreads();
+    __shared__ uint32_t cnt_all;
+    if (threadIdx.x < 64) {  // exclusive scan of the 256 (j, wave) counts, 4 per lane
+        uint32_t e[4], s = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int idx = 4 * lane + q;
+            e[q] = woff[idx / NW][idx % NW];
+            s += e[q];
+        }
+        uint32_t u = s;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(u, off);
+            if (lane >= off) u += y;
+        }
+        uint32_t run = u - s;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int idx = 4 * lane + q;
+            woff[idx / NW][idx % NW] = run;
+            run += e[q];
+        }
+        if (lane == 63) cnt_all = u;
+    }
+    __syncthreads();
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        if ((m[j] >> lane) & 1ull) {
+            const uint32_t slot = woff[j][w] + (uint32_t)__popcll(m[j] & below);
+            if (slot < (uint32_t)a.k) write_one(a, t, (int)slot, c[j]);
+        }
+    }
+    const uint32_t cnt = cnt_all < (uint32_t)a.k ? cnt_all : (uint32_t)a.k;
+    write_pad(a, t, cnt);
+}
+
+// ---------------------------------------------------------------- longer rows
+struct RowState {
+    uint32_t n_sure;
+    uint32_t n_cand;
+    uint32_t pad[30];  // one 128-byte line per row
+};
+
+struct WsView {
+    RowState* st;     // [nq]
+    uint32_t* hist;   // [nq][2048]
+    uint64_t* sure;   // [nq][2048]
+    uint64_t* cand;   // [nq][cap]
+    int64_t cap;
+    int64_t chunks;
+};
+
+__host__ __device__ inline WsView ws_view(void* ws, int32_t nq, int64_t cap) {
+    WsView v;
+    v.cap = cap > 0 ? cap : 1;
+    v.chunks = (v.cap + kChunk - 1) / kChunk;
+    char* p = (char*)ws;
+    v.st = (RowState*)p;
+    p += align_up((size_t)nq * sizeof(RowState));
+    v.hist = (uint32_t*)p;
+    p += align_up((size_t)nq * kHistBins * 4);
+    v.sure = (uint64_t*)p;
+    p += align_up((size_t)nq * kMaxK * 8);
+    v.cand = (uint64_t*)p;
+    return v;
+}
+
+__global__ __launch_bounds__(kLargeThreads) void select_hist_kernel(SelectArgs a, WsView v) {
+    __shared__ Hist<kLargeThreads> H;
     const int64_t t = blockIdx.y;
     const RowInfo ri = row_info(a, t);
     const int64_t c0 = (int64_t)blockIdx.x * kChunk;
     if (c0 >= ri.len) return;  // uniform per block
-    for (int b = threadIdx.x; b < kHistBins; b += blockDim.x) h[b] = 0u;
+    uint64_t c[kPer];
+    load_composites<kPer>(a, t, ri, c0 + threadIdx.x, kLargeThreads, c);
+    hist_clear_own(H);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+        if (c[j]) hist_add(H, (uint32_t)(c[j] >> 53));
     __syncthreads();
-    const int64_t c1 = c0 + kChunk < ri.len ? c0 + kChunk : ri.len;
-    for (int64_t i = c0 + threadIdx.x; i < c1; i += blockDim.x) {
-        const uint32_t k = key_at(a, t, i, ri);
-        if (eligible(k)) atomicAdd(&h[k >> 21], 1u);
-    }
+    hist_reduce(H);
     __syncthreads();
-    for (int b = threadIdx.x; b < kHistBins; b += blockDim.x)
-        if (h[b]) atomicAdd(&v.hist[t * kHistBins + b], h[b]);
+    uint32_t* rh = v.hist + t * kHistBins;
+    for (int b = threadIdx.x; b < kHistBins; b += kLargeThreads)
+        if (H.h[hidx(b)]) atomicAdd(&rh[b], H.h[hidx(b)]);
 }
 
-// threshold digit of a 2048-bin histogram: the largest d with sum_{b >= d} h[b] >= need;
-// returns -1 (and *above = total) when the total is below need. 256 threads, 8 bins each.
-__device__ int find_threshold(const uint32_t* h, uint32_t need, uint32_t* above, uint32_t* total, uint32_t* scratch,
-                              int* result) {
-    const int tid = threadIdx.x;
-    uint32_t part = 0;
-    for (int b = 0; b < 8; ++b) part += h[tid * 8 + b];
-    scratch[tid] = part;
-    if (tid == 0) *result = -1;
-    __syncthreads();
-    // suffix sums over the 256 partials (inclusive), Hillis-Steele
-    for (int off = 1; off < 256; off <<= 1) {
-        uint32_t x = (tid + off < 256) ? scratch[tid + off] : 0u;
-        __syncthreads();
-        scratch[tid] += x;
-        __syncthreads();
-    }
-    uint32_t cum = scratch[tid] - part;  // elements in bins above this thread's range
-    const uint32_t tot = scratch[0];
-    for (int b = tid * 8 + 7; b >= tid * 8; --b) {
-        if (cum < need && cum + h[b] >= need) {
-            *result = b;
-            *above = cum;
-        }
-        cum += h[b];
-    }
-    __syncthreads();
-    if (*result < 0 && tid == 0) *above = tot;
-    *total = tot;
-    __syncthreads();
-    return *result;
-}
-
+// append with one LDS atomic per wavefront
 __device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
     const uint64_t m = __ballot(pred);
     if (m == 0) return 0;
@@ -161,184 +468,160 @@ __device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
     return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
 }
 
-__global__ __launch_bounds__(256) void select_filter_kernel(SelectArgs a, WsView v) {
-    __shared__ uint32_t h[kHistBins];
-    __shared__ uint32_t scratch[256];
-    __shared__ uint32_t above, total;
-    __shared__ int thr;
+__global__ __launch_bounds__(kLargeThreads) void select_filter_kernel(SelectArgs a, WsView v) {
+    __shared__ uint32_t h[kPadBins];
+    __shared__ uint64_t lsure[kMaxK];
+    __shared__ uint64_t lcand[kChunk];
+    __shared__ Sel sel;
+    __shared__ uint32_t ns, nc, bs, bc;
     const int64_t t = blockIdx.y;
     const RowInfo ri = row_info(a, t);
     const int64_t c0 = (int64_t)blockIdx.x * kChunk;
-    if (c0 >= ri.len && blockIdx.x != 0) return;
-    for (int b = threadIdx.x; b < kHistBins; b += blockDim.x) h[b] = v.hist[t * kHistBins + b];
+    if (c0 >= ri.len) return;  // uniform per block
+    uint64_t c[kPer];
+    load_composites<kPer>(a, t, ri, c0 + threadIdx.x, kLargeThreads, c);
+    const uint32_t* rh = v.hist + t * kHistBins;
+    for (int b = threadIdx.x; b < kHistBins; b += kLargeThreads) h[hidx(b)] = rh[b];
+    if (threadIdx.x == 0) {
+        ns = 0;
+        nc = 0;
+    }
     __syncthreads();
-    const int b1 = find_threshold(h, (uint32_t)a.k, &above, &total, scratch, &thr);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        v.ctl[t].thr_bin = b1;
-        v.ctl[t].total = total;
+    block_threshold(h, (uint32_t)a.k, sel);
+    const int d1 = sel.digit;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int bin = c[j] ? (int)(c[j] >> 53) : -2;
+        const bool sure = c[j] != 0 && bin > d1;
+        const bool on = c[j] != 0 && bin == d1;
+        const uint32_t ps = wave_append(sure, &ns);
+        const uint32_t pc = wave_append(on, &nc);
+        if (sure && ps < (uint32_t)kMaxK) lsure[ps] = c[j];
+        if (on) lcand[pc] = c[j];
     }
-    const int64_t c1 = c0 + kChunk < ri.len ? c0 + kChunk : ri.len;
-    // iterate in wave-uniform trip counts so that ballots see the whole wave
-    for (int64_t i0 = c0; i0 < c1; i0 += blockDim.x) {
-        const int64_t i = i0 + threadIdx.x;
-        uint32_t k = 0;
-        if (i < c1) k = key_at(a, t, i, ri);
-        const bool ok = i < c1 && eligible(k);
-        const int bin = (int)(k >> 21);
-        const bool sure = ok && bin > b1;
-        const bool cand = ok && bin == b1;
-        const uint32_t ps = wave_append(sure, &v.ctl[t].sure);
-        const uint32_t pc = wave_append(cand, &v.ctl[t].cand);
-        if (sure || cand) {
-            const uint64_t comp = ((uint64_t)k << 32) | (uint64_t)(~pos_at(a, t, i));
-            if (sure) v.sel[t * a.k + ps] = comp;
-            else if ((int64_t)pc < v.cap) v.cand[t * v.cap + pc] = comp;
-        }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        bs = ns ? atomicAdd(&v.st[t].n_sure, ns) : 0u;
+        bc = nc ? atomicAdd(&v.st[t].n_cand, nc) : 0u;
     }
+    __syncthreads();
+    uint64_t* gs = v.sure + t * kMaxK;
+    uint64_t* gc = v.cand + t * v.cap;
+    for (uint32_t i = threadIdx.x; i < ns; i += kLargeThreads)
+        if (bs + i < (uint32_t)kMaxK) gs[bs + i] = lsure[i];
+    for (uint32_t i = threadIdx.x; i < nc; i += kLargeThreads) gc[bc + i] = lcand[i];
 }
 
 __global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(SelectArgs a, WsView v) {
-    __shared__ uint64_t keep[kMaxK];
-    __shared__ uint32_t h[kHistBins];
-    __shared__ uint32_t scratch[256];
-    __shared__ uint32_t nkeep, above, total;
-    __shared__ int thr;
+    __shared__ Hist<kFinishThreads> H;
+    __shared__ uint64_t out[kMaxK];
+    __shared__ uint32_t bits[kBitmapMax / 32];
+    __shared__ uint32_t wsum[64];
+    __shared__ Sel sel;
+    __shared__ uint32_t ns, nall;
     const int64_t t = blockIdx.x;
-    const int tid = threadIdx.x;
-    const RowCtl ctl = v.ctl[t];
-    const uint32_t nsure = ctl.sure;
-    uint32_t ncand = ctl.cand;
-    if ((int64_t)ncand > v.cap) ncand = (uint32_t)v.cap;
-    for (uint32_t i = tid; i < nsure; i += blockDim.x) keep[i] = v.sel[t * a.k + i];
-    if (tid == 0) nkeep = nsure;
+    uint32_t* rh = v.hist + t * kHistBins;
+    for (int b = threadIdx.x; b < kHistBins; b += kFinishThreads) H.h[hidx(b)] = rh[b];
+    const uint32_t nsure = v.st[t].n_sure;
+    const uint32_t ncand = v.st[t].n_cand;
+    const uint64_t* gs = v.sure + t * kMaxK;
+    const uint64_t* gc = v.cand + t * v.cap;
+    for (uint32_t i = threadIdx.x; i < nsure && i < (uint32_t)kMaxK; i += kFinishThreads) out[i] = gs[i];
+    if (threadIdx.x == 0) ns = nsure < (uint32_t)kMaxK ? nsure : (uint32_t)kMaxK;
     __syncthreads();
-    uint32_t need = ctl.thr_bin >= 0 ? (uint32_t)a.k - nsure : 0u;
-    const uint64_t* cand = v.cand + t * v.cap;
-    // composite bits below the top 11 (which all candidates share): digits 52..42, 41..31,
-    // 30..20, 19..9, 8..0
-    uint64_t prefix = 0, mask = 0;
-    const int shifts[5] = {42, 31, 20, 9, 0};
-    const int widths[5] = {11, 11, 11, 11, 9};
-    for (int p = 0; p < 5 && need > 0; ++p) {
-        const int sh = shifts[p];
-        const uint64_t dm = ((uint64_t)1 << widths[p]) - 1;
-        for (int b = tid; b < kHistBins; b += blockDim.x) h[b] = 0u;
-        __syncthreads();
-        for (uint32_t i = tid; i < ncand; i += blockDim.x) {
-            const uint64_t c = cand[i];
-            if (((c ^ prefix) & mask) == 0) atomicAdd(&h[(c >> sh) & dm], 1u);
-        }
-        __syncthreads();
-        // threshold digit with 256 threads over 2048 bins
-        int d = -1;
-        if (tid < 256) {
-            uint32_t part = 0;
-            for (int b = 0; b < 8; ++b) part += h[tid * 8 + b];
-            scratch[tid] = part;
-            if (tid == 0) thr = -1;
-        }
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {
-            uint32_t x = 0;
-            if (tid < 256) x = (tid + off < 256) ? scratch[tid + off] : 0u;
-            __syncthreads();
-            if (tid < 256) scratch[tid] += x;
-            __syncthreads();
-        }
-        if (tid < 256) {
-            uint32_t cum = scratch[tid];
-            uint32_t part = 0;
-            for (int b = 0; b < 8; ++b) part += h[tid * 8 + b];
-            cum -= part;
-            for (int b = tid * 8 + 7; b >= tid * 8; --b) {
-                if (cum < need && cum + h[b] >= need) {
-                    thr = b;
-                    above = cum;
-                }
-                cum += h[b];
-            }
-        }
-        __syncthreads();
-        d = thr;  // always found: candidates matching the prefix number at least `need`
-        const bool take_eq = (h[d] == need - above);
-        for (uint32_t i = tid; i < ncand; i += blockDim.x) {
-            const uint64_t c = cand[i];
-            if (((c ^ prefix) & mask) != 0) continue;
-            const int dig = (int)((c >> sh) & dm);
-            if (dig > d || (take_eq && dig == d)) {
-                const uint32_t slot = atomicAdd(&nkeep, 1u);
-                if (slot < kMaxK) keep[slot] = c;
-            }
-        }
-        __syncthreads();
-        if (take_eq) need = 0;
-        else {
-            need -= above;
-            prefix |= (uint64_t)d << sh;
-            mask |= dm << sh;
-        }
-        __syncthreads();
+    block_threshold(H.h, (uint32_t)a.k, sel);
+    const int d1 = sel.digit;
+    // leave the row histogram and counters cleared for the next call
+    for (int b = threadIdx.x; b < kHistBins; b += kFinishThreads) rh[b] = 0u;
+    if (threadIdx.x == 0) {
+        v.st[t].n_sure = 0u;
+        v.st[t].n_cand = 0u;
     }
-    const uint32_t cnt = nkeep < (uint32_t)a.k ? nkeep : (uint32_t)a.k;
-    // sort: descending composite (rank order) or, in pool mode, ascending block id
-    int N = 1;
-    while (N < (int)cnt) N <<= 1;
-    for (int i = tid; i < N; i += blockDim.x) {
-        if (i >= (int)cnt) keep[i] = a.pool_mode ? ~0ull : 0ull;
-        else if (a.pool_mode) keep[i] = (uint64_t)(uint32_t)(~(uint32_t)keep[i]);
+    if (d1 >= 0 && nsure < (uint32_t)a.k) {
+        auto each = [&](auto&& f) {
+            for (uint32_t i = threadIdx.x; i < ncand; i += kFinishThreads) f(gc[i]);
+        };
+        uint32_t need = (uint32_t)a.k - nsure;
+        uint64_t prefix = (uint64_t)d1 << 53, mask = ~0ull << 53, T = ~0ull;
+        for (int p = 1; p < 6; ++p)
+            if (radix_pass<kFinishThreads>(each, p, need, prefix, mask, T, H, sel)) break;
+        for (uint32_t i0 = 0; i0 < ncand; i0 += kFinishThreads) {
+            const uint32_t i = i0 + threadIdx.x;
+            const uint64_t c = i < ncand ? gc[i] : 0ull;
+            const bool take = c != 0 && c >= T;
+            const uint32_t slot = wave_append(take, &ns);
+            if (take && slot < (uint32_t)kMaxK) out[slot] = c;
+        }
     }
     __syncthreads();
-    for (int size = 2; size <= N; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < N / 2; i += blockDim.x) {
-                const int lo = 2 * stride * (i / stride) + (i % stride);
-                const int hi = lo + stride;
-                const bool up = (lo & size) == 0;
-                const uint64_t x = keep[lo], y = keep[hi];
-                if ((x > y) == up) {
-                    keep[lo] = y;
-                    keep[hi] = x;
-                }
+    const uint32_t cnt = ns < (uint32_t)a.k ? ns : (uint32_t)a.k;
+    const RowInfo ri = row_info(a, t);
+    if (a.pool_mode && ri.len <= kBitmapMax) {
+        // ascending block ids through an LDS bitmap and a block-wide prefix sum
+        const int words = (int)((ri.len + 31) / 32);
+        for (int i = threadIdx.x; i < words; i += kFinishThreads) bits[i] = 0u;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < cnt; i += kFinishThreads) {
+            const uint32_t pos = comp_pos(out[i]);
+            atomicOr(&bits[pos >> 5], 1u << (pos & 31));
+        }
+        __syncthreads();
+        const int per = (words + kFinishThreads - 1) / kFinishThreads;
+        const int w0 = threadIdx.x * per;
+        uint32_t mine = 0;
+        for (int q = 0; q < per; ++q)
+            if (w0 + q < words) mine += (uint32_t)__popc(bits[w0 + q]);
+        uint32_t base = block_exclusive_scan<kFinishThreads>(mine, wsum, &nall);
+        for (int q = 0; q < per; ++q) {
+            if (w0 + q >= words) break;
+            uint32_t b = bits[w0 + q];
+            while (b) {
+                const int bit = __ffs(b) - 1;
+                b &= b - 1;
+                a.out_idx[t * a.out_stride + base] = (w0 + q) * 32 + bit;
+                ++base;
             }
-            __syncthreads();
+        }
+    } else {
+        // ascending position: sort (pos, key) pairs
+        int N = 1;
+        while (N < (int)cnt) N <<= 1;
+        for (int i = threadIdx.x; i < N; i += kFinishThreads)
+            out[i] = i < (int)cnt ? (((uint64_t)comp_pos(out[i]) << 32) | comp_key(out[i])) : ~0ull;
+        __syncthreads();
+        block_sort<kFinishThreads>(out, N);
+        for (int i = threadIdx.x; i < (int)cnt; i += kFinishThreads) {
+            const uint64_t pk = out[i];
+            a.out_idx[t * a.out_stride + i] = (int32_t)(uint32_t)(pk >> 32);
+            if (a.out_val && !a.pool_mode) a.out_val[t * a.out_stride + i] = key_value((uint32_t)pk);
         }
     }
-    int32_t* oi = a.out_idx + t * a.out_stride;
-    for (int i = tid; i < a.pad_to; i += blockDim.x) {
-        if (i < (int)cnt) {
-            if (a.pool_mode) {
-                oi[i] = (int32_t)keep[i];
-            } else {
-                const uint64_t c = keep[N - 1 - i];
-                oi[i] = (int32_t)(~(uint32_t)c);
-                if (a.out_val) a.out_val[t * a.out_stride + i] = key_value((uint32_t)(c >> 32));
-            }
-        } else {
-            oi[i] = -1;
-            if (a.out_val && !a.pool_mode) a.out_val[t * a.out_stride + i] = -INFINITY;
-        }
-    }
-    if (a.out_count && tid == 0) a.out_count[t] = (int32_t)cnt;
+    write_pad(a, t, cnt);
 }
 
 }  // namespace
 
 size_t select_workspace_bytes(int32_t nq, int64_t cap, int32_t k) {
-    if (nq <= 0 || cap < 0 || k <= 0) return 0;
-    return align_up((size_t)nq * kHistBins * 4) + align_up((size_t)nq * sizeof(RowCtl)) +
-           align_up((size_t)nq * k * 8) + align_up((size_t)nq * (size_t)(cap > 0 ? cap : 1) * 8);
+    (void)k;
+    if (nq <= 0 || cap < 0) return 0;
+    if (cap <= kSmallRow) return 256;
+    const WsView v = ws_view(nullptr, nq, cap);
+    return align_up((size_t)nq * sizeof(RowState)) + align_up((size_t)nq * kHistBins * 4) +
+           align_up((size_t)nq * kMaxK * 8) + align_up((size_t)nq * (size_t)v.cap * 8);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
     if (a.nq <= 0) return hipSuccess;
-    const int64_t cap = a.pool_mode ? (a.max_n + kBlock - 1) / kBlock : a.max_n;
-    const WsView v = ws_view(a.ws, a.nq, cap > 0 ? cap : 1, a.k);
-    const int64_t nclear = (int64_t)a.nq * kHistBins;
-    hipLaunchKernelGGL(select_clear_kernel, dim3((unsigned)((nclear + 255) / 256)), dim3(256), 0, stream, v.hist,
-                       v.ctl, a.nq);
-    const int64_t gx = cap > 0 ? (cap + kChunk - 1) / kChunk : 1;
-    hipLaunchKernelGGL(select_hist_kernel, dim3((unsigned)gx, (unsigned)a.nq), dim3(256), 0, stream, a, v);
-    hipLaunchKernelGGL(select_filter_kernel, dim3((unsigned)gx, (unsigned)a.nq), dim3(256), 0, stream, a, v);
+    const int64_t cap = row_cap(a);
+    if (cap <= kSmallRow) {
+        hipLaunchKernelGGL(select_small_kernel, dim3((unsigned)a.nq), dim3(kSmallThreads), 0, stream, a);
+        return hipGetLastError();
+    }
+    const WsView v = ws_view(a.ws, a.nq, cap);
+    hipLaunchKernelGGL(select_hist_kernel, dim3((unsigned)v.chunks, (unsigned)a.nq), dim3(kLargeThreads), 0, stream,
+                       a, v);
+    hipLaunchKernelGGL(select_filter_kernel, dim3((unsigned)v.chunks, (unsigned)a.nq), dim3(kLargeThreads), 0,
+                       stream, a, v);
     hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)a.nq), dim3(kFinishThreads), 0, stream, a, v);
     return hipGetLastError();
 }
