@@ -38,6 +38,22 @@ def scan_bytes(n_vis, nq: int) -> int:
     return keys * 68 + nq * (32 * 68 + 32 * 4) + blocks * 4
 
 
+def measured_traffic() -> int | None:
+    """HBM bytes per scan launch from the committed rocprofv3 counter record, or None when the
+    scan's sources have changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "score_full_fullscan_1m_traffic.json")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256()
+        for f in rec["source_files"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        return int(rec["traffic_bytes_per_launch"]) if h.hexdigest() == rec["source_sha256"] else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, max_queries: int = 8) -> dict:
     """The oracle (plain C, threaded over queries) on a bounded sample: the Full layer of the
     first min(8, cores) sequences of the same workload (score every key, top-512, block maxima,
@@ -79,6 +95,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="fullscan_1m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only copy 512 MiB device-to-device 5 times (calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the indexer shards by "
@@ -94,6 +112,14 @@ def main() -> int:
     from top_fp4_lightning_amd import pipeline
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": src.numel(), "launches": 5}), flush=True)
+        return 0
     wl = synth.config(args.workload)
     t = time.perf_counter()
     dev = pipeline.DeviceWorkload.from_workload(wl)
@@ -156,7 +182,7 @@ def main() -> int:
         "full_scan_entries_per_s": int(sum(n_vis)) / (scan_ms / 1000.0),
         "scan_ms": scan_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "score_full_kernel", "algorithmic_bytes_per_launch": sb},
     }
     if not args.no_cpu_baseline:
