@@ -88,6 +88,51 @@ def cpu_baseline(wl, max_queries: int = 8) -> dict:
             "seconds": round(dt, 3)}
 
 
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak, published
+
+
+def bench_prefill(wl, args) -> int:
+    """Chunked prefill: 4096 consecutive queries on 131072 keys, causal; the step is quantise q,
+    the many-query scan (block maxima), top-512 blocks per query, re-score of those 4096 keys,
+    final top-512. The roofline is the scan's FP4 matrix throughput."""
+    import numpy as np
+    import torch
+
+    from top_fp4_lightning_amd import pipeline
+
+    t = time.perf_counter()
+    dev = pipeline.DeviceWorkload.from_workload(wl, group=wl.nq)
+    torch.cuda.synchronize()
+    log(f"workload {wl.name}: {wl.nq} queries, {wl.total_keys} keys; setup {time.perf_counter() - t:.1f} s")
+    plan = pipeline.PrefillPlan(dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        plan.run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        plan.run(events=evs[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1000.0 / args.steps
+    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    pairs = int(wl.n_vis.sum())
+    flop = 2.0 * 4096.0 * pairs
+    achieved = flop / (scan_ms / 1000.0) / 1e12
+    print(json.dumps({
+        "metric": "prefill (query, key) pairs scored/s; % of FP4 MFMA roofline",
+        "value": pairs / (ms_step / 1000.0), "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp4", "data": "synthetic",
+        "config": {"workload": "prefill_128k: 4096 queries x 131072 keys, causal (query i sees <= 126976+i)"},
+        "queries_per_s": wl.nq / (ms_step / 1000.0), "scan_ms": scan_ms,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_FP4_PEAK_TFLOPS, "traffic": None, "kernel": "score_multi_kernel",
+                     "algorithmic_flop_per_launch": flop},
+    }), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +166,8 @@ def main() -> int:
         print(json.dumps({"copy_probe_bytes": src.numel(), "launches": 5}), flush=True)
         return 0
     wl = synth.config(args.workload)
+    if args.workload == "prefill_128k":
+        return bench_prefill(wl, args)
     t = time.perf_counter()
     dev = pipeline.DeviceWorkload.from_workload(wl)
     torch.cuda.synchronize()

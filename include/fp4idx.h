@@ -105,7 +105,8 @@ idx_status idx_quantize_q(const uint16_t* x_bf16, int64_t rows, const int8_t* si
  *   nq      : number of queries, >= 0.
  *   group   : >= 1 and divides nq; each run of `group` consecutive queries shares one key range
  *             (k_base equal within a run): 1 for batched decode, the chunk size for prefill.
- *   max_n   : host upper bound on n_vis, >= 0 (sizes the launch grid).
+ *   max_n   : host upper bound on n_vis, 0 .. 2^24 (sizes the launch grid; one query's key range
+ *             is addressed with 32-bit offsets).
  *   q_codes, q_scales : device, [nq][32][64] and [nq][32][4] (16- and 4-byte aligned).
  *   w       : device fp32 [nq][32], 4-byte aligned.
  *   scores  : device fp32 [nq][score_stride] or NULL; written for s < n_t only.
@@ -154,7 +155,8 @@ idx_status idx_build_pool(const float* block_max, int64_t bm_stride, const int32
  * 16384 x 4096 MACs per query independent of context length; and the remark that the saving
  * needs a kernel that reads only pooled keys, after the mask-form reference code).
  *
- *   k_codes, k_scales, k_base, n_vis, q_codes, q_scales, w : as for idx_score_full (group 1).
+ *   k_codes, k_scales, k_base, n_vis, q_codes, q_scales, w : as for idx_score_full (group 1);
+ *                 n_vis values above 2^24 are clamped to 2^24.
  *   blocks      : device int32 [nq][blocks_stride]; block ids (any order) of query t are
  *                 blocks[t][0 .. block_count[t] - 1].
  *   block_count : device int32 [nq]; values are clamped to [0, max_blocks].

@@ -91,7 +91,9 @@ def test_score_full_validation(fx):
     bad = list(good); bad[2] = None
     assert f(*bad) == fx.IDX_EINVAL
     bad = list(good); bad[6] = -5
-    assert f(*bad) == fx.IDX_EINVAL
+    assert f(*bad) == fx.IDX_EUNSUPPORTED
+    bad = list(good); bad[6] = (1 << 24) + 1; bad[11] = 1 << 25; bad[13] = 1 << 22
+    assert f(*bad) == fx.IDX_EUNSUPPORTED
 
 
 def test_build_pool_validation(fx):

@@ -17,6 +17,9 @@ FLAGS = [
     "-shared",
     # keep the compiler from emitting packed fp32 VALU ops (v_pk_fma/mul/add_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-instruction results in ordinary VGPRs: the epilogue reads them without
+    # v_accvgpr_read copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

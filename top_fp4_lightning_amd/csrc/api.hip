@@ -78,7 +78,7 @@ idx_status idx_score_full(const uint8_t* k_codes, const uint8_t* k_scales, const
                           const uint8_t* q_scales, const float* w, float* scores, int64_t score_stride,
                           float* block_max, int64_t bm_stride, float* head_dots, void* stream) {
     REQUIRE(nq >= 0 && nq <= kMaxQueries, IDX_EUNSUPPORTED, "idx_score_full: nq=%d out of [0, 65535]", nq);
-    REQUIRE(max_n >= 0 && max_n <= kMaxN, IDX_EINVAL, "idx_score_full: max_n=%lld out of [0, 2^30]",
+    REQUIRE(max_n >= 0 && max_n <= kMaxScanKeys, IDX_EUNSUPPORTED, "idx_score_full: max_n=%lld out of [0, 2^24]",
             (long long)max_n);
     REQUIRE(group >= 1 && (nq == 0 || nq % group == 0), IDX_EINVAL, "idx_score_full: group=%d must divide nq=%d",
             group, nq);

@@ -13,6 +13,9 @@ constexpr int kGroups = 4;      // UE8M0 scales per row (groups of 32)
 constexpr int kBlock = 8;       // positions per pool block
 constexpr int kMaxK = 2048;
 constexpr int kHistBins = 2048; // 11-bit radix digits
+// Largest key range one query may scan: key offsets inside a range are 32-bit byte offsets
+// (64 B per key) in buffer descriptors.
+constexpr int64_t kMaxScanKeys = (int64_t)1 << 24;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));

@@ -12,6 +12,11 @@
 // four lane rows are then combined for four tiles at once with two permlane32 swaps and one
 // permlane16 swap, which leaves the score of key l of the 64-key step in lane l.
 //
+// Keys are read with buffer loads through a descriptor that spans exactly one query's key range:
+// reads past the range return zeros (zero codes contribute nothing), so there are no per-lane
+// branches around loads, offsets are 32-bit, and the next step's loads stay in flight while the
+// current step computes.
+//
 // The scale-FP4 MFMA returns exact per-head dots whenever the per-block scale exponents of a
 // dot stay within a narrow range (exact sums of FP4 products below 2^24 ulps of the smallest
 // block), which the UE8M0 encoding of real activations satisfies; the head sum is fp32.
@@ -20,9 +25,16 @@
 namespace fp4idx {
 namespace {
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format, range checked
+
+// FP4 operands occupy the low four registers of the instruction's 8-register operand
+__device__ __forceinline__ v8i widen(v4i x) { return v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0}; }
+
 struct QRegs {
-    v8i a[2];     // heads 0-15 and 16-31: this lane's 32-element block of head (l % 16) + 16h
-    int sc[2];    // its UE8M0 scale byte
+    v4i a[2];       // heads 0-15 and 16-31: this lane's 32-element block of head (l % 16) + 16h
+    int sc[2];      // its UE8M0 scale byte
     float w[2][4];  // weights of output heads 16h + 4 * (l / 16) + i
 };
 
@@ -33,29 +45,49 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_codes, 
     for (int h = 0; h < 2; ++h) {
         const int head = 16 * h + r;
         const uint4 c = *reinterpret_cast<const uint4*>(q_codes + ((t * kHeads + head) * kRowBytes + g * 16));
-        q.a[h] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+        q.a[h] = v4i{(int)c.x, (int)c.y, (int)c.z, (int)c.w};
         q.sc[h] = (int)q_scales[(t * kHeads + head) * kGroups + g];
 #pragma unroll
         for (int i = 0; i < 4; ++i) q.w[h][i] = w[t * kHeads + 16 * h + 4 * g + i];
     }
 }
 
-// B operand of one tile: key rows given per lane (row < 0: absent key, zero contribution)
+// one query's (or group's) key rows [base, base + n) as two range-checked buffers
+struct KeyRange {
+    __amdgpu_buffer_rsrc_t codes;
+    __amdgpu_buffer_rsrc_t scales;
+};
+
+__device__ __forceinline__ KeyRange key_range(const uint8_t* k_codes, const uint8_t* k_scales, int64_t base,
+                                              int64_t n) {
+    KeyRange r;
+    r.codes = __builtin_amdgcn_make_buffer_rsrc((void*)(k_codes + base * kRowBytes), 0, (int)(n * kRowBytes),
+                                                kRsrcWord3);
+    r.scales = __builtin_amdgcn_make_buffer_rsrc((void*)(k_scales + base * kGroups), 0, (int)(n * kGroups),
+                                                 kRsrcWord3);
+    return r;
+}
+
+constexpr uint32_t kAbsent = 0x3ffffffu;  // a key index past every range: its loads read zeros
+
+// B operand of one tile
 struct KTile {
-    v8i b;
+    v4i b;
     int sc;
 };
 
-__device__ __forceinline__ void load_key(const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
-                                         int64_t row, int g, KTile& kt) {
-    if (row >= 0) {
-        const uint4 c = *reinterpret_cast<const uint4*>(k_codes + row * kRowBytes + g * 16);
-        kt.b = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-        kt.sc = (int)k_scales[row * kGroups + g];
-    } else {
-        kt.b = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        kt.sc = 0;
-    }
+// cache policy of key loads: kStream marks them non-temporal (a scan reads each key once and
+// should not displace reusable lines), kReuse keeps the default policy (pooled keys are re-read by
+// later layers, prefill keys by other query tiles)
+constexpr int kReuse = 0;
+constexpr int kStream = 2;
+
+template <int POLICY>
+__device__ __forceinline__ void load_key(const KeyRange& kr, uint32_t e, int g, KTile& kt) {
+    const auto c =
+        __builtin_amdgcn_raw_buffer_load_b128(kr.codes, e * (uint32_t)kRowBytes + (uint32_t)g * 16u, 0, POLICY);
+    kt.b = v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+    kt.sc = (int)__builtin_amdgcn_raw_buffer_load_b8(kr.scales, e * (uint32_t)kGroups + (uint32_t)g, 0, POLICY);
 }
 
 struct TileOut {
@@ -66,8 +98,13 @@ __device__ __forceinline__ void mfma_tile(const QRegs& q, const KTile& kt, TileO
     const v4f z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-        o.d[h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q.a[h], kt.b, z, 4, 4, 0, q.sc[h], 0, kt.sc);
+        o.d[h] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(q.a[h]), widen(kt.b), z, 4, 4, 0, q.sc[h], 0,
+                                                                  kt.sc);
 }
+
+// ReLU on the fp32 bit pattern: as a signed integer every negative float (and -0) is below 0,
+// every positive float keeps its bits; one integer max, no NaN canonicalisation
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // this lane's partial score: sum over its 8 heads of w * ReLU(d), fixed order
 __device__ __forceinline__ float lane_partial(const QRegs& q, const TileOut& o) {
@@ -75,7 +112,7 @@ __device__ __forceinline__ float lane_partial(const QRegs& q, const TileOut& o) 
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p = fmaf(q.w[h][i], fmaxf(o.d[h][i], 0.0f), p);
+        for (int i = 0; i < 4; ++i) p = fmaf(q.w[h][i], relu(o.d[h][i]), p);
     return p;
 }
 
@@ -91,16 +128,23 @@ __device__ __forceinline__ float combine4(float p0, float p1, float p2, float p3
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+// lane move inside the data-parallel-primitive network (no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// maximum over each aligned group of 8 lanes, in all 8 lanes
 __device__ __forceinline__ float max8(float v) {
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]: partner lane ^ 1
+    v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]: partner lane ^ 2
+    v = fmaxf(v, dpp_mov<0x141>(v));  // row_half_mirror: lane i <-> 7 - i, i.e. the other quad
     return v;
 }
 
 // --------------------------------------------------------------------------------------------
 // Full-layer scan, one query per key range. Grid: x = chunks of 4 waves x ITERS x 64 keys,
-// y = queries. Keys past n_t are neither read nor scored.
+// y = queries. Keys past n_t are not scored (their loads read zeros).
 template <int ITERS>
 __global__ __launch_bounds__(256) void score_full_kernel(ScoreArgs a) {
     const int lane = threadIdx.x & 63;
@@ -113,25 +157,20 @@ __global__ __launch_bounds__(256) void score_full_kernel(ScoreArgs a) {
 
     QRegs q;
     load_query(a.q_codes, a.q_scales, a.w, t, lane, q);
-    const int64_t base = a.k_base[t];
+    const KeyRange kr = key_range(a.k_codes, a.k_scales, a.k_base[t], n);
     const int g = lane >> 4, r = lane & 15;
+    float* bm_row = a.block_max ? a.block_max + t * a.bm_stride : nullptr;
+    float* sc_row = a.scores ? a.scores + t * a.score_stride : nullptr;
 
     KTile cur[4], nxt[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int64_t e = e_begin + 16 * u + r;
-        load_key(a.k_codes, a.k_scales, e < n ? base + e : -1, g, cur[u]);
-    }
+    for (int u = 0; u < 4; ++u) load_key<kStream>(kr, (uint32_t)(e_begin + 16 * u + r), g, cur[u]);
     for (int it = 0; it < ITERS; ++it) {
         const int64_t e0 = e_begin + (int64_t)it * 64;
         if (e0 >= n) break;
-        const int64_t e1 = e0 + 64;
-        if (it + 1 < ITERS && e1 < n) {
+        if (it + 1 < ITERS) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t e = e1 + 16 * u + r;
-                load_key(a.k_codes, a.k_scales, e < n ? base + e : -1, g, nxt[u]);
-            }
+            for (int u = 0; u < 4; ++u) load_key<kStream>(kr, (uint32_t)(e0 + 64 + 16 * u + r), g, nxt[u]);
         }
         float p[4];
 #pragma unroll
@@ -150,14 +189,13 @@ __global__ __launch_bounds__(256) void score_full_kernel(ScoreArgs a) {
                 }
             }
         }
-        float s = combine4(p[0], p[1], p[2], p[3]);
+        const float s = combine4(p[0], p[1], p[2], p[3]);
         const int64_t e = e0 + lane;
         const bool valid = e < n;
-        if (a.scores && valid) a.scores[t * a.score_stride + e] = s;
-        if (a.block_max) {
+        if (sc_row && valid) sc_row[e] = s;
+        if (bm_row) {
             const float m = max8(valid ? s : -INFINITY);
-            const int64_t b = e >> 3;
-            if ((lane & 7) == 0 && e < n) a.block_max[t * a.bm_stride + b] = m;
+            if ((lane & 7) == 0 && valid) bm_row[e >> 3] = m;
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
@@ -178,41 +216,32 @@ __global__ __launch_bounds__(256) void score_gather_kernel(GatherArgs a) {
     int64_t cnt = a.block_count[t];
     cnt = cnt < 0 ? 0 : (cnt > a.max_blocks ? a.max_blocks : cnt);
     int64_t n = a.n_vis[t];
-    n = n < 0 ? 0 : n;
+    n = n < 0 ? 0 : (n > kMaxScanKeys ? kMaxScanKeys : n);
 
     QRegs q;
     load_query(a.q_codes, a.q_scales, a.w, t, lane, q);
-    const int64_t base = a.k_base[t];
+    const KeyRange kr = key_range(a.k_codes, a.k_scales, a.k_base[t], n);
     const int g = lane >> 4, r = lane & 15;
     const int32_t* blk = a.blocks + t * a.blocks_stride;
 
-    // position of slot s, or -1 if absent
-    auto pos_of = [&](int64_t s) -> int64_t {
-        if (s >= slots) return -1;
+    // key index of slot s within the query's range, kAbsent if the slot is empty
+    auto pos_of = [&](int64_t s) -> uint32_t {
         const int64_t i = s >> 3;
-        if (i >= cnt) return -1;
+        if (s >= slots || i >= cnt) return kAbsent;
         const int64_t b = blk[i];
-        if (b < 0) return -1;
         const int64_t pos = b * kBlock + (s & 7);
-        return pos < n ? pos : -1;
+        return (b >= 0 && pos < n) ? (uint32_t)pos : kAbsent;
     };
 
     KTile cur[4], nxt[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int64_t pos = pos_of(s_begin + 16 * u + r);
-        load_key(a.k_codes, a.k_scales, pos >= 0 ? base + pos : -1, g, cur[u]);
-    }
+    for (int u = 0; u < 4; ++u) load_key<kReuse>(kr, pos_of(s_begin + 16 * u + r), g, cur[u]);
     for (int it = 0; it < ITERS; ++it) {
         const int64_t s0 = s_begin + (int64_t)it * 64;
         if (s0 >= slots) break;
-        const int64_t s1 = s0 + 64;
-        if (it + 1 < ITERS && s1 < slots) {
+        if (it + 1 < ITERS) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t pos = pos_of(s1 + 16 * u + r);
-                load_key(a.k_codes, a.k_scales, pos >= 0 ? base + pos : -1, g, nxt[u]);
-            }
+            for (int u = 0; u < 4; ++u) load_key<kReuse>(kr, pos_of(s0 + 64 + 16 * u + r), g, nxt[u]);
         }
         float p[4];
 #pragma unroll
@@ -222,7 +251,7 @@ __global__ __launch_bounds__(256) void score_gather_kernel(GatherArgs a) {
             p[u] = lane_partial(q, o);
             if (a.head_dots) {
                 const int64_t s = s0 + 16 * u + r;
-                if (pos_of(s) >= 0) {
+                if (pos_of(s) != kAbsent) {
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -233,7 +262,74 @@ __global__ __launch_bounds__(256) void score_gather_kernel(GatherArgs a) {
         }
         const float sc = combine4(p[0], p[1], p[2], p[3]);
         const int64_t s = s0 + lane;
-        if (s < slots) a.scores[t * a.score_stride + s] = pos_of(s) >= 0 ? sc : -INFINITY;
+        if (s < slots) a.scores[t * a.score_stride + s] = pos_of(s) != kAbsent ? sc : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+    }
+}
+
+// --------------------------------------------------------------------------------------------
+// Many queries sharing one key range (chunked prefill, speculative decode). Each wave keeps QW
+// queries in registers and applies every 16-key tile it loads to all of them, so a tile's MFMA
+// work is QW times the single-query scan's; the four waves of a block take consecutive queries
+// and the same key chunk. Grid: x = query tiles of 4*QW queries (fastest, so that concurrently
+// running blocks share a key chunk in L2), y = key chunks of KT*64 keys, z = groups.
+template <int QW, int KT>
+__global__ __launch_bounds__(256) void score_multi_kernel(ScoreArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t g0 = (int64_t)blockIdx.z * a.group;  // first query of the group
+    const int64_t qw0 = g0 + ((int64_t)blockIdx.x * 4 + wave) * QW;
+    const int64_t g_end = g0 + a.group;
+    const int64_t e_begin = (int64_t)blockIdx.y * (KT * 64);
+
+    int64_t nq_[QW];
+    int64_t nmax = 0;
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+        const int64_t qq = qw0 + i;
+        int64_t n = qq < g_end ? (int64_t)a.n_vis[qq] : 0;
+        n = n < 0 ? 0 : (n > a.max_n ? a.max_n : n);
+        nq_[i] = n;
+        nmax = n > nmax ? n : nmax;
+    }
+    if (e_begin >= nmax) return;  // uniform per wave
+
+    QRegs q[QW];
+#pragma unroll
+    for (int i = 0; i < QW; ++i) load_query(a.q_codes, a.q_scales, a.w, qw0 + i < g_end ? qw0 + i : g0, lane, q[i]);
+    const KeyRange kr = key_range(a.k_codes, a.k_scales, a.k_base[g0], nmax);
+    const int g = lane >> 4, r = lane & 15;
+
+    KTile cur[4], nxt[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load_key<kReuse>(kr, (uint32_t)(e_begin + 16 * u + r), g, cur[u]);
+    for (int it = 0; it < KT; ++it) {
+        const int64_t e0 = e_begin + (int64_t)it * 64;
+        if (e0 >= nmax) break;
+        if (it + 1 < KT) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) load_key<kReuse>(kr, (uint32_t)(e0 + 64 + 16 * u + r), g, nxt[u]);
+        }
+        const int64_t e = e0 + lane;
+#pragma unroll
+        for (int i = 0; i < QW; ++i) {
+            float p[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                TileOut o;
+                mfma_tile(q[i], cur[u], o);
+                p[u] = lane_partial(q[i], o);
+            }
+            const float sc = combine4(p[0], p[1], p[2], p[3]);
+            const int64_t qq = qw0 + i;
+            const bool valid = e < nq_[i];
+            if (a.scores && valid) a.scores[qq * a.score_stride + e] = sc;
+            if (a.block_max) {
+                const float m = max8(valid ? sc : -INFINITY);
+                if ((lane & 7) == 0 && valid) a.block_max[qq * a.bm_stride + (e >> 3)] = m;
+            }
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
     }
@@ -241,11 +337,22 @@ __global__ __launch_bounds__(256) void score_gather_kernel(GatherArgs a) {
 
 constexpr int kScanIters = 4;    // 4 waves x 4 steps x 64 keys = 1024 keys per block
 constexpr int kGatherIters = 1;
+constexpr int kMultiQ = 4;       // queries per wave in the many-query scan
+constexpr int kMultiIters = 16;  // 64-key steps per block (1024 keys)
 
 }  // namespace
 
 hipError_t launch_score_full(const ScoreArgs& a, hipStream_t stream) {
     if (a.nq <= 0 || a.max_n <= 0) return hipSuccess;
+    if (a.group > 1 && a.head_dots == nullptr) {
+        const int64_t qtile = 4 * kMultiQ;
+        const int64_t gx = (a.group + qtile - 1) / qtile;
+        const int64_t gy = (a.max_n + kMultiIters * 64 - 1) / (kMultiIters * 64);
+        const int64_t gz = a.nq / a.group;
+        hipLaunchKernelGGL((score_multi_kernel<kMultiQ, kMultiIters>), dim3((unsigned)gx, (unsigned)gy, (unsigned)gz),
+                           dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
     const int64_t per_block = 4 * kScanIters * 64;
     const int64_t gx = (a.max_n + per_block - 1) / per_block;
     hipLaunchKernelGGL(score_full_kernel<kScanIters>, dim3((unsigned)gx, (unsigned)a.nq), dim3(256), 0, stream, a);

@@ -158,11 +158,15 @@ class PrefillPlan:
         self.ws_blocks = workspace(IDX_OP_TOPK, nq, max(nb, 1), k, device=d)
         self.ws_final = workspace(IDX_OP_TOPK, nq, max(self.kb * BLOCK, 1), k, device=d)
 
-    def run(self, stream=None):
+    def run(self, stream=None, events=None):
         dv = self.dev
         idx_quantize_q(dv.q[0], dv.signs, self.q_codes, self.q_scales, stream=stream)
+        if events is not None:
+            events[0].record()
         idx_score_full(dv.k_codes, dv.k_scales, dv.k_base, dv.n_vis, self.q_codes, self.q_scales, dv.w[0], dv.max_n,
                        group=dv.group, block_max=self.block_max, stream=stream)
+        if events is not None:
+            events[1].record()
         idx_topk(self.block_max, self.nb, self.k, self.top_blocks, self.ws_blocks, n_valid=self.n_blocks,
                  stream=stream)
         idx_score_pool_gather(dv.k_codes, dv.k_scales, dv.k_base, dv.n_vis, self.top_blocks, self.block_count,
