@@ -13,7 +13,9 @@
 // The winners are written in ascending position order (the natural order for gathering the
 // selected keys afterwards), with no sort on the hot paths:
 //  - rows of at most 16384 values: one 1024-thread block per row, 16 composites per thread in
-//    registers (one launch); winners are compacted in slot order with wavefront ballots, which is
+//    registers (one launch); the first radix pass runs over the whole row, the remaining ones on
+//    the elements of the threshold digit only (copied to LDS, one wavefront, no block barriers);
+//    winners are compacted in slot order with wavefront ballots, which is
 //    position order when the optional block map is ascending (as the pool and this function
 //    produce);
 //  - longer rows (candidate pool over 2^17 block maxima, full score rows): three launches over
@@ -31,7 +33,6 @@ namespace fp4idx {
 namespace {
 
 constexpr int kSmallRow = 16384;
-constexpr int kSmallThreads = 1024;
 constexpr int kPer = 16;  // values per thread
 constexpr int kLargeThreads = 256;
 constexpr int kChunk = kLargeThreads * kPer;
@@ -159,46 +160,42 @@ __device__ __forceinline__ void hist_reduce(Hist<NT>& H) {
 }
 
 // Threshold digit of the padded histogram h: the largest d with sum_{b >= d} h[b] >= need
-// (d = -1 when the total is below need); `above` = count in bins above d. Wave 0 computes;
-// ends with a barrier. Lane l owns bins [32l, 32l + 32).
+// (d = -1 when the total is below need); `above` = count in bins above d. Computed by one whole
+// wavefront (lane l owns bins [32l, 32l + 32)); every lane returns the result.
+__device__ Sel wave_threshold(const uint32_t* h, uint32_t need) {
+    const int lane = threadIdx.x & 63;
+    uint32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) s += h[33 * lane + j];
+    uint32_t suf = s;  // inclusive suffix sum over lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_down(suf, off);
+        if (lane + off < 64) suf += o;
+    }
+    const uint32_t total = __shfl(suf, 0);
+    if (total < need) return Sel{-1, total};
+    const uint64_t own = __ballot(suf - s < need && need <= suf);
+    const int L = __ffsll((unsigned long long)own) - 1;
+    const uint32_t aboveL = __shfl(suf - s, L);
+    const uint32_t v = lane < 32 ? h[33 * L + lane] : 0u;
+    uint32_t vs = v;  // inclusive suffix over lanes 0..31
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+        const uint32_t o = __shfl_down(vs, off);
+        if (lane + off < 32) vs += o;
+    }
+    const bool hit = lane < 32 && aboveL + vs >= need && aboveL + vs - v < need;
+    const uint64_t hm = __ballot(hit);
+    const int J = __ffsll((unsigned long long)hm) - 1;
+    return Sel{32 * L + J, aboveL + __shfl(vs - v, J)};
+}
+
+// the same, computed by wave 0 for the whole block; ends with a barrier
 __device__ void block_threshold(const uint32_t* h, uint32_t need, Sel& sel) {
     if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        uint32_t s = 0;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) s += h[33 * lane + j];
-        uint32_t suf = s;  // inclusive suffix sum over lanes
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t o = __shfl_down(suf, off);
-            if (lane + off < 64) suf += o;
-        }
-        const uint32_t total = __shfl(suf, 0);
-        if (total < need) {
-            if (lane == 0) {
-                sel.digit = -1;
-                sel.above = total;
-            }
-        } else {
-            const uint64_t own = __ballot(suf - s < need && need <= suf);
-            const int L = __ffsll((unsigned long long)own) - 1;
-            const uint32_t aboveL = __shfl(suf - s, L);
-            const uint32_t v = lane < 32 ? h[33 * L + lane] : 0u;
-            uint32_t vs = v;  // inclusive suffix over lanes 0..31
-#pragma unroll
-            for (int off = 1; off < 32; off <<= 1) {
-                const uint32_t o = __shfl_down(vs, off);
-                if (lane + off < 32) vs += o;
-            }
-            const bool hit = lane < 32 && aboveL + vs >= need && aboveL + vs - v < need;
-            const uint64_t hm = __ballot(hit);
-            const int J = __ffsll((unsigned long long)hm) - 1;
-            const uint32_t aboveJ = aboveL + __shfl(vs - v, J);
-            if (lane == 0) {
-                sel.digit = 32 * L + J;
-                sel.above = aboveJ;
-            }
-        }
+        const Sel r = wave_threshold(h, need);
+        if (threadIdx.x == 0) sel = r;
     }
     __syncthreads();
 }
@@ -341,35 +338,91 @@ __device__ __forceinline__ void write_pad(const SelectArgs& a, int64_t t, uint32
 }
 
 // ---------------------------------------------------------------- rows of <= 16384 values
-__global__ __launch_bounds__(kSmallThreads) void select_small_kernel(SelectArgs a) {
-    constexpr int NW = kSmallThreads / 64;
-    __shared__ Hist<kSmallThreads> H;
+constexpr int kRowThreads = 1024;
+constexpr int kRowPer = kSmallRow / kRowThreads;  // 16 composites per thread, in registers
+constexpr int kListCap = 4096;                    // LDS candidates for the wave-level passes
+
+// Radix passes p0..5 by one wavefront over a candidate list in LDS (no block barriers); same
+// contract as radix_pass. h is a padded 2048-bin histogram owned by this wave.
+__device__ uint64_t wave_radix(const uint64_t* list, uint32_t n, uint32_t need, int p0, uint64_t prefix,
+                               uint64_t mask, uint32_t* h) {
+    const int lane = threadIdx.x & 63;
+    for (int p = p0; p < 6; ++p) {
+        const int shf = kShift[p];
+        const uint64_t dm = ((uint64_t)1 << kWidth[p]) - 1;
+        for (int b = lane; b < kPadBins; b += 64) h[b] = 0u;
+        __threadfence_block();
+        for (uint32_t i = lane; i < n; i += 64) {
+            const uint64_t c = list[i];
+            if (((c ^ prefix) & mask) == 0) atomicAdd(&h[hidx((int)((c >> shf) & dm))], 1u);
+        }
+        __threadfence_block();
+        const Sel r = wave_threshold(h, need);
+        if (r.digit < 0) return 1ull;
+        if (h[hidx(r.digit)] == need - r.above) return prefix | ((uint64_t)r.digit << shf);
+        need -= r.above;
+        prefix |= (uint64_t)r.digit << shf;
+        mask |= dm << shf;
+    }
+    return prefix;
+}
+
+__global__ __launch_bounds__(kRowThreads) void select_small_kernel(SelectArgs a) {
+    constexpr int NW = kRowThreads / 64;
+    __shared__ Hist<kRowThreads> H;
     __shared__ Sel sel;
-    __shared__ uint32_t woff[kPer][NW];
+    __shared__ uint32_t woff[kRowPer][NW];
+    __shared__ uint32_t cnt_all, n_list;
+    __shared__ uint64_t T_sh;
+    // the candidate list reuses the per-wave histogram words, dead after the first pass
+    static_assert(sizeof(H.hw) >= kListCap * sizeof(uint64_t), "candidate list must fit in the histogram space");
+    uint64_t* list = reinterpret_cast<uint64_t*>(&H.hw[0][0]);
     const int64_t t = blockIdx.x;
     const RowInfo ri = row_info(a, t);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint64_t c[kPer];
-    load_composites<kPer>(a, t, ri, threadIdx.x, kSmallThreads, c);
+    uint64_t c[kRowPer];
+    load_composites<kRowPer>(a, t, ri, threadIdx.x, kRowThreads, c);
     auto each = [&](auto&& f) {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) f(c[j]);
+        for (int j = 0; j < kRowPer; ++j) f(c[j]);
     };
     uint32_t need = (uint32_t)a.k;
     uint64_t prefix = 0ull, mask = 0ull, T = ~0ull;
-    if (ri.len > 0)
-        for (int p = 0; p < 6; ++p)
-            if (radix_pass<kSmallThreads>(each, p, need, prefix, mask, T, H, sel)) break;
-    // ordered compaction: slot order (j, wave, lane)
-    uint64_t m[kPer];
+    if (threadIdx.x == 0) n_list = 0;
+    if (ri.len > 0 && !radix_pass<kRowThreads>(each, 0, need, prefix, mask, T, H, sel)) {
+        // the threshold digit holds H.h[d] candidates; finish on them alone when they fit
+        const uint32_t ncand = H.h[hidx(sel.digit)];
+        if (ncand <= (uint32_t)kListCap) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+            for (int j = 0; j < kRowPer; ++j) {
+                const bool on = c[j] != 0 && ((c[j] ^ prefix) & mask) == 0;
+                const uint64_t m = __ballot(on);
+                uint32_t base = 0;
+                if (lane == 0 && m) base = atomicAdd(&n_list, (uint32_t)__popcll(m));
+                base = __shfl(base, 0);
+                if (on) list[base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull))] = c[j];
+            }
+            __syncthreads();
+            if (threadIdx.x < 64) {
+                const uint64_t r = wave_radix(list, n_list, need, 1, prefix, mask, H.h);
+                if (threadIdx.x == 0) T_sh = r;
+            }
+            __syncthreads();
+            T = T_sh;
+        } else {
+            for (int p = 1; p < 6; ++p)
+                if (radix_pass<kRowThreads>(each, p, need, prefix, mask, T, H, sel)) break;
+        }
+    }
+    // ordered compaction: slot order (j, wave, lane)
+    uint64_t m[kRowPer];
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) {
         m[j] = __ballot(c[j] != 0 && c[j] >= T);
         if (lane == 0) woff[j][w] = (uint32_t)__popcll(m[j]);
     }
     __syncthreads();
-    __shared__ uint32_t cnt_all;
-    if (threadIdx.x < 64) {  // exclusive scan of the 256 (j, wave) counts, 4 per lane
+    if (threadIdx.x < 64) {  // exclusive scan of the kRowPer * NW (j, wave) counts, 4 per lane
         uint32_t e[4], s = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -395,7 +448,7 @@ __global__ __launch_bounds__(kSmallThreads) void select_small_kernel(SelectArgs 
     __syncthreads();
     const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+    for (int j = 0; j < kRowPer; ++j) {
         if ((m[j] >> lane) & 1ull) {
             const uint32_t slot = woff[j][w] + (uint32_t)__popcll(m[j] & below);
             if (slot < (uint32_t)a.k) write_one(a, t, (int)slot, c[j]);
@@ -614,7 +667,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
     if (a.nq <= 0) return hipSuccess;
     const int64_t cap = row_cap(a);
     if (cap <= kSmallRow) {
-        hipLaunchKernelGGL(select_small_kernel, dim3((unsigned)a.nq), dim3(kSmallThreads), 0, stream, a);
+        hipLaunchKernelGGL(select_small_kernel, dim3((unsigned)a.nq), dim3(kRowThreads), 0, stream, a);
         return hipGetLastError();
     }
     const WsView v = ws_view(a.ws, a.nq, cap);
