@@ -372,7 +372,8 @@ __global__ __launch_bounds__(kRowThreads) void select_small_kernel(SelectArgs a)
     __shared__ Hist<kRowThreads> H;
     __shared__ Sel sel;
     __shared__ uint32_t woff[kRowPer][NW];
-    __shared__ uint32_t cnt_all, n_list;
+    __shared__ uint32_t cnt_all;
+    __shared__ uint32_t seg_cnt[NW];
     __shared__ uint64_t T_sh;
     // the candidate list reuses the per-wave histogram words, dead after the first pass
     static_assert(sizeof(H.hw) >= kListCap * sizeof(uint64_t), "candidate list must fit in the histogram space");
@@ -388,23 +389,31 @@ __global__ __launch_bounds__(kRowThreads) void select_small_kernel(SelectArgs a)
     };
     uint32_t need = (uint32_t)a.k;
     uint64_t prefix = 0ull, mask = 0ull, T = ~0ull;
-    if (threadIdx.x == 0) n_list = 0;
     if (ri.len > 0 && !radix_pass<kRowThreads>(each, 0, need, prefix, mask, T, H, sel)) {
-        // the threshold digit holds H.h[d] candidates; finish on them alone when they fit
+        // the threshold digit holds H.h[d] candidates; when they fit, they are packed into one LDS
+        // list (per-wave offsets from ballot counts, no atomics) and one wavefront finishes on them
         const uint32_t ncand = H.h[hidx(sel.digit)];
         if (ncand <= (uint32_t)kListCap) {
+            const uint64_t below = (1ull << lane) - 1ull;
+            uint64_t m[kRowPer];
+            uint32_t mine = 0;
 #pragma unroll
             for (int j = 0; j < kRowPer; ++j) {
-                const bool on = c[j] != 0 && ((c[j] ^ prefix) & mask) == 0;
-                const uint64_t m = __ballot(on);
-                uint32_t base = 0;
-                if (lane == 0 && m) base = atomicAdd(&n_list, (uint32_t)__popcll(m));
-                base = __shfl(base, 0);
-                if (on) list[base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull))] = c[j];
+                m[j] = __ballot(c[j] != 0 && ((c[j] ^ prefix) & mask) == 0);
+                mine += (uint32_t)__popcll(m[j]);
+            }
+            if (lane == 0) seg_cnt[w] = mine;
+            __syncthreads();
+            uint32_t base = 0;
+            for (int sg = 0; sg < w; ++sg) base += seg_cnt[sg];
+#pragma unroll
+            for (int j = 0; j < kRowPer; ++j) {
+                if ((m[j] >> lane) & 1ull) list[base + (uint32_t)__popcll(m[j] & below)] = c[j];
+                base += (uint32_t)__popcll(m[j]);
             }
             __syncthreads();
             if (threadIdx.x < 64) {
-                const uint64_t r = wave_radix(list, n_list, need, 1, prefix, mask, H.h);
+                const uint64_t r = wave_radix(list, ncand, need, 1, prefix, mask, H.h);
                 if (threadIdx.x == 0) T_sh = r;
             }
             __syncthreads();
