@@ -38,12 +38,13 @@ def scan_bytes(n_vis, nq: int) -> int:
     return keys * 68 + nq * (32 * 68 + 32 * 4) + blocks * 4
 
 
-def measured_traffic() -> int | None:
-    """HBM bytes per scan launch from the committed rocprofv3 counter record, or None when the
-    scan's sources have changed since the counters were taken."""
+def measured_traffic(record: str) -> int | None:
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter record
+    (profiles/<record>.json), or None when the kernel's sources have changed since the counters
+    were taken."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", "score_full_fullscan_1m_traffic.json")
+    path = os.path.join(ROOT, "profiles", record + ".json")
     try:
         rec = json.load(open(path))
         h = hashlib.sha256()
@@ -127,7 +128,8 @@ def bench_prefill(wl, args) -> int:
         "config": {"workload": "prefill_128k: 4096 queries x 131072 keys, causal (query i sees <= 126976+i)"},
         "queries_per_s": wl.nq / (ms_step / 1000.0), "scan_ms": scan_ms,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_FP4_PEAK_TFLOPS, "traffic": None, "kernel": "score_multi_kernel",
+                     "frac": achieved / MFMA_FP4_PEAK_TFLOPS,
+                     "traffic": measured_traffic("score_multi_prefill_128k_traffic"), "kernel": "score_multi_kernel",
                      "algorithmic_flop_per_launch": flop},
     }), flush=True)
     return 0
@@ -229,7 +231,7 @@ def main() -> int:
         "full_scan_entries_per_s": int(sum(n_vis)) / (scan_ms / 1000.0),
         "scan_ms": scan_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("score_full_fullscan_1m_traffic"),
                      "kernel": "score_full_kernel", "algorithmic_bytes_per_launch": sb},
     }
     if not args.no_cpu_baseline:

@@ -7,7 +7,7 @@ import tempfile
 from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["api.hip", "quantize.hip", "score.hip", "select.hip"]
+SOURCES = ["api.hip", "quantize.hip", "score.hip", "score_multi.hip", "select.hip"]
 OUT = os.path.join(HERE, "libfp4idx.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -26,7 +26,7 @@ FLAGS = [
 # Scoring never meets a NaN: FP4 codes are finite, E8M0 scales stop at 2^127 (the NaN byte 255
 # is never produced and is rejected by contract), weights are finite. Without NaN semantics a
 # float max needs no operand canonicalisation and folds the cross-lane move into itself.
-PER_FILE = {"score.hip": ["-fno-honor-nans"]}
+PER_FILE = {"score.hip": ["-fno-honor-nans"], "score_multi.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, obj: str) -> None:

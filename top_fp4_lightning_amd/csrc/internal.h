@@ -42,6 +42,8 @@ struct ScoreArgs {
     float* head_dots;
 };
 hipError_t launch_score_full(const ScoreArgs& a, hipStream_t stream);
+// many queries per key range (group > 1, no per-head output): the scan above dispatches to it
+hipError_t launch_score_multi(const ScoreArgs& a, hipStream_t stream);
 
 struct GatherArgs {
     const uint8_t* k_codes;

@@ -1,0 +1,277 @@
+// Many-query indexer scan on gfx950 (chunked prefill, speculative decode): every query of a group
+// shares one key range; scores and / or block-8 maxima as in the single-query scan.
+#include "score_common.h"
+
+#include <type_traits>
+
+namespace fp4idx {
+namespace {
+
+#ifndef FP4IDX_MULTI_WAVES
+#define FP4IDX_MULTI_WAVES 1
+#endif
+// Many queries sharing one key range (chunked prefill, speculative decode).
+//
+// Work unit: a tile of 32 keys against all 32 heads of one query as two
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4 ops (the second accumulating onto the first). Lane l supplies
+// row / column l % 32 and, in op k (k = 0, 1), the FP4 block 2 * (l / 32) + k: so op 0 contracts
+// blocks 0 and 2, op 1 blocks 1 and 3, and a lane reads the 32 contiguous code bytes of its key's
+// half row plus the two scale bytes of that half (selected per op by the scale byte-select).
+// Output: lane l holds key l % 32 for the 16 heads 8 * (j / 4) + 4 * (l / 32) + j % 4
+// (j = 0..15). On this chip a 32x32x64 op overlaps the ReLU epilogue better than two
+// 16x16x128 ops and leaves half the matrix instructions.
+//
+// The head sum is taken in the same order as the single-query scan, so both paths give
+// bit-identical scores: each lane keeps the two 8-head chains (4g .. 4g+3, 16+4g .. 16+4g+3)
+// for g = l / 32 and g + 2, adds them, and one cross-half add completes the key.
+//
+// Each wave keeps QW queries in registers and applies every tile it loads to all of them; the
+// four waves of a block take consecutive queries and the same key chunk. Grid: x = query tiles
+// of 4*QW queries (fastest, so that concurrently running blocks share a key chunk in L2),
+// y = key chunks of KT*64 keys, z = groups. SCORES / BMAX select the outputs at compile time.
+// Steps whose 64 keys are visible to every query of the wave run without masks; the remaining
+// steps run a masked copy.
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+struct QRegs32 {
+    v4i a[2];     // op k: this lane's FP4 block 2 * (l / 32) + k of head l % 32
+    int sc;       // byte k: that block's UE8M0 scale
+    float w[16];  // weights of the output rows held by this lane
+};
+
+__device__ __forceinline__ void load_query32(const uint8_t* __restrict__ q_codes,
+                                             const uint8_t* __restrict__ q_scales, const float* __restrict__ w,
+                                             int64_t t, int lane, QRegs32& q) {
+    const int head = lane & 31, h = lane >> 5;
+    const uint8_t* row = q_codes + (t * kHeads + head) * kRowBytes + 32 * h;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint4 c = *reinterpret_cast<const uint4*>(row + 16 * k);
+        q.a[k] = v4i{(int)c.x, (int)c.y, (int)c.z, (int)c.w};
+    }
+    const uint8_t* srow = q_scales + (t * kHeads + head) * kGroups + 2 * h;
+    q.sc = (int)srow[0] | ((int)srow[1] << 8);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) q.w[j] = w[t * kHeads + 8 * (j / 4) + 4 * h + (j % 4)];
+}
+
+struct KTile32 {
+    v4i b[2];
+    int sc;
+};
+
+__device__ __forceinline__ void load_key32(const KeyRange& kr, uint32_t e, int h, KTile32& kt) {
+    const uint32_t off = e * (uint32_t)kRowBytes + (uint32_t)h * 32u;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const auto c = __builtin_amdgcn_raw_buffer_load_b128(kr.codes, off + 16u * k, 0, kReuse);
+        kt.b[k] = v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+    }
+    kt.sc = (int)__builtin_amdgcn_raw_buffer_load_b16(kr.scales, e * (uint32_t)kGroups + (uint32_t)h * 2u, 0, kReuse);
+}
+
+__device__ __forceinline__ v16f mfma_tile32(const QRegs32& q, const KTile32& kt) {
+    v16f z;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) z[j] = 0.0f;
+    const v16f t =
+        __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(q.a[0]), widen(kt.b[0]), z, 4, 4, 0, q.sc, 0, kt.sc);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(q.a[1]), widen(kt.b[1]), t, 4, 4, 1, q.sc, 1, kt.sc);
+}
+
+// this lane's partial: chain over rows j = 0-3, 8-11 plus chain over rows 4-7, 12-15
+__device__ __forceinline__ float lane_partial32(const QRegs32& q, const v16f& o) {
+    float pa = 0.0f, pb = 0.0f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pa = fmaf(q.w[8 * b + i], relu(o[8 * b + i]), pa);
+            pb = fmaf(q.w[8 * b + 4 + i], relu(o[8 * b + 4 + i]), pb);
+        }
+    return pa + pb;
+}
+
+// two tiles' partials -> in lane l the score of key l of the 64-key step
+__device__ __forceinline__ float combine2(float p0, float p1) {
+    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Keys of one 64-key step are staged in LDS once per block: 4 KiB of codes (16-byte chunks
+// XOR-swizzled so that eight consecutive keys fall on distinct bank groups, both for the
+// staging writes and the operand reads) and 256 bytes of scales. Two buffers alternate; one
+// barrier per step orders the writes of step s + 1 before its reads and the reads of step s - 1
+// before the buffer is overwritten. Control flow around the barriers is uniform per block.
+constexpr int kStepKeys = 64;
+constexpr int kStageCodes = kStepKeys * kRowBytes;  // bytes of codes per step
+constexpr int kStageScales = kStepKeys * kGroups;
+
+struct StageBuf {
+    alignas(16) uint8_t codes[2][kStageCodes];
+    alignas(16) uint32_t scales[2][kStepKeys];
+};
+
+// LDS byte offset of 16-byte chunk p (0..3) of key kk (0..63) of a step
+__device__ __forceinline__ uint32_t stage_chunk(int kk, int p) {
+    return (uint32_t)(kk * 4 + (p ^ ((kk >> 1) & 3))) * 16u;
+}
+
+template <int QW, int KT, bool SCORES, bool BMAX>
+__global__ __launch_bounds__(256, FP4IDX_MULTI_WAVES) void score_multi_kernel(ScoreArgs a) {
+    __shared__ StageBuf sb;
+    const int lane = threadIdx.x & 63;
+    // wave index as a uniform value: query bounds, key range and descriptors stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t g0 = (int64_t)blockIdx.z * a.group;  // first query of the group
+    const int64_t qb0 = g0 + (int64_t)blockIdx.x * 4 * QW;  // first query of the block
+    const int64_t qw0 = qb0 + (int64_t)wave * QW;
+    const int64_t g_end = g0 + a.group;
+    const int e_begin = (int)blockIdx.y * (KT * kStepKeys);  // key ranges are below 2^24
+
+    // visible-key counts: the block's maximum bounds the staging (uniform per block), the wave's
+    // bounds decide which steps it scores and which run masked (uniform per wave)
+    auto nvis = [&](int64_t qq) -> int {
+        int64_t n = qq < g_end ? (int64_t)a.n_vis[qq] : 0;
+        return (int)(n < 0 ? 0 : (n > a.max_n ? a.max_n : n));
+    };
+    int nb_max = 0;
+#pragma unroll
+    for (int i = 0; i < 4 * QW; ++i) {
+        const int n = nvis(qb0 + i);
+        nb_max = n > nb_max ? n : nb_max;
+    }
+    if (e_begin >= nb_max) return;  // uniform per block
+    int nq_[QW];
+    int nmax = 0, nmin = INT32_MAX;
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+        nq_[i] = nvis(qw0 + i);
+        nmax = nq_[i] > nmax ? nq_[i] : nmax;
+        nmin = nq_[i] < nmin ? nq_[i] : nmin;
+    }
+    const int e_stop = e_begin + KT * kStepKeys < nb_max ? e_begin + KT * kStepKeys : nb_max;
+    const int n_steps = (e_stop - e_begin + kStepKeys - 1) / kStepKeys;
+
+    QRegs32 q[QW];
+#pragma unroll
+    for (int i = 0; i < QW; ++i)
+        load_query32(a.q_codes, a.q_scales, a.w, qw0 + i < g_end ? qw0 + i : g0, lane, q[i]);
+    const KeyRange kr = key_range(a.k_codes, a.k_scales, a.k_base[g0], nb_max);
+    const int h = lane >> 5, c = lane & 31;
+    // per-query output rows; a query past the group has n = 0 and never stores
+    float* srow[QW];
+    float* brow[QW];
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+        const int64_t qq = qw0 + i < g_end ? qw0 + i : g0;
+        srow[i] = SCORES ? a.scores + qq * a.score_stride : nullptr;
+        brow[i] = BMAX ? a.block_max + qq * a.bm_stride : nullptr;
+    }
+
+    // staging: thread T carries 16-byte chunk T % 4 of key T / 4; wave 0 also the scale words
+    const int T = threadIdx.x;
+    const uint32_t st_code = stage_chunk(T >> 2, T & 3);
+    v4i st_c;
+    uint32_t st_s = 0;
+    auto stage_load = [&](int e0) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(kr.codes, (uint32_t)e0 * kRowBytes + (uint32_t)T * 16u, 0,
+                                                            kReuse);
+        st_c = v4i{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+        if (wave == 0)
+            st_s = __builtin_amdgcn_raw_buffer_load_b32(kr.scales, (uint32_t)(e0 + T) * kGroups, 0, kReuse);
+    };
+    auto stage_store = [&](int buf) {
+        *reinterpret_cast<v4i*>(__builtin_assume_aligned(&sb.codes[buf][st_code], 16)) = st_c;
+        if (wave == 0) sb.scales[buf][T] = st_s;
+    };
+    // operands of tile u (keys 32u .. 32u + 31 of the step) from buffer buf
+    auto read_tiles = [&](int buf, KTile32 (&t)[2]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int kk = 32 * u + c;
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                t[u].b[k] = *reinterpret_cast<const v4i*>(
+                    __builtin_assume_aligned(&sb.codes[buf][stage_chunk(kk, 2 * h + k)], 16));
+            t[u].sc = (int)reinterpret_cast<const uint16_t*>(&sb.scales[buf][kk])[h];
+        }
+    };
+
+    // score one 64-key step for every query; MASKED steps drop keys past each query's count
+    auto step = [&](const KTile32 (&t)[2], int e0, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+        const int el = e0 + lane;
+#pragma unroll
+        for (int i = 0; i < QW; ++i) {
+            const v16f o0 = mfma_tile32(q[i], t[0]);
+            const v16f o1 = mfma_tile32(q[i], t[1]);
+            const float sc = combine2(lane_partial32(q[i], o0), lane_partial32(q[i], o1));
+            if (!MASKED) {
+                if (SCORES) srow[i][el] = sc;
+                // all eight lanes of a block hold its maximum and store the same value
+                if (BMAX) brow[i][el >> 3] = max8(sc);
+            } else {
+                const bool valid = el < nq_[i];
+                if (SCORES && valid) srow[i][el] = sc;
+                if (BMAX) {
+                    const float m = max8(valid ? sc : -INFINITY);
+                    if (valid) brow[i][el >> 3] = m;
+                }
+            }
+            // one query's matrix results live at a time: keeps the wave within the register
+            // budget of four waves per SIMD (other waves hide the matrix latency)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    stage_load(e_begin);
+    stage_store(0);
+    if (n_steps > 1) stage_load(e_begin + kStepKeys);
+    __syncthreads();
+    for (int it = 0; it < n_steps; ++it) {
+        const int e0 = e_begin + it * kStepKeys;
+        if (e0 < nmax) {  // uniform per wave
+            KTile32 t[2];
+            read_tiles(it & 1, t);
+            if (e0 + kStepKeys <= nmin)
+                step(t, e0, std::false_type{});
+            else
+                step(t, e0, std::true_type{});
+        }
+        if (it + 1 < n_steps) stage_store((it + 1) & 1);
+        if (it + 2 < n_steps) stage_load(e0 + 2 * kStepKeys);
+        __syncthreads();
+    }
+}
+
+#ifndef FP4IDX_MULTI_QW
+#define FP4IDX_MULTI_QW 2
+#endif
+#ifndef FP4IDX_MULTI_KT
+#define FP4IDX_MULTI_KT 32
+#endif
+// queries per wave in the many-query scan: two keep a wave within 128 registers, i.e. four
+// waves per SIMD, which hide the matrix-result latency of each other
+constexpr int kMultiQ = FP4IDX_MULTI_QW;
+constexpr int kMultiIters = FP4IDX_MULTI_KT;  // 64-key steps per block (2048 keys)
+
+}  // namespace
+
+hipError_t launch_score_multi(const ScoreArgs& a, hipStream_t stream) {
+    if (a.nq <= 0 || a.max_n <= 0) return hipSuccess;
+    const int64_t qtile = 4 * kMultiQ;
+    const int64_t gx = (a.group + qtile - 1) / qtile;
+    const int64_t gy = (a.max_n + kMultiIters * 64 - 1) / (kMultiIters * 64);
+    const int64_t gz = a.nq / a.group;
+    const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)gz);
+    if (a.scores && a.block_max)
+        hipLaunchKernelGGL((score_multi_kernel<kMultiQ, kMultiIters, true, true>), grid, dim3(256), 0, stream, a);
+    else if (a.scores)
+        hipLaunchKernelGGL((score_multi_kernel<kMultiQ, kMultiIters, true, false>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((score_multi_kernel<kMultiQ, kMultiIters, false, true>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace fp4idx
