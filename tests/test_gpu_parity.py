@@ -121,7 +121,11 @@ def make_rows(rng, nq, n, kind):
 
 @pytest.mark.parametrize("n,k,kind", [(1000, 512, "normal"), (70000, 512, "normal"), (5000, 2048, "ties"),
                                       (3000, 7, "ties"), (20000, 512, "equal"), (9000, 2048, "neginf"),
-                                      (300, 512, "normal"), (1 << 20, 512, "normal"), (1, 1, "normal")])
+                                      (300, 512, "normal"), (1 << 20, 512, "normal"), (1, 1, "normal"),
+                                      # block-size boundaries of the short-row kernel (256 / 512 / 1024
+                                      # threads), and candidate lists beyond the smaller LDS list
+                                      (4096, 512, "normal"), (4097, 512, "normal"), (8192, 2048, "normal"),
+                                      (8193, 512, "ties"), (4096, 2048, "equal"), (4000, 512, "ties")])
 def test_topk_exact(fx, n, k, kind):
     rng = np.random.default_rng(n + k)
     nq = 3
@@ -141,6 +145,26 @@ def test_topk_exact(fx, n, k, kind):
         assert (out[t, cnt:] == -1).all()
         assert np.array_equal(oval[t, :cnt], vals[t, ref_pos])
         assert np.all(np.isneginf(oval[t, cnt:]))
+
+
+@pytest.mark.parametrize("n,k", [(4096, 512), (8000, 512), (16384, 512)])
+def test_topk_many_rows(fx, n, k):
+    # many rows per launch (the prefill shape), each with its own valid length
+    rng = np.random.default_rng(n * 7 + k)
+    nq = 777
+    vals = rng.standard_normal((nq, n)).astype(np.float32)
+    nvalid = rng.integers(0, n + 1, nq).astype(np.int32)
+    nvalid[:3] = [n, 0, k - 1]
+    ws = fx.workspace(fx.IDX_OP_TOPK, nq, n, k)
+    out = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
+    fx.idx_topk(torch.from_numpy(vals).cuda(), n, k, out, ws, n_valid=torch.from_numpy(nvalid).cuda())
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for t in range(nq):
+        ref = oracle.topk(vals[t, :nvalid[t]].astype(np.float64), k)
+        cnt = int((ref >= 0).sum())
+        assert np.array_equal(out[t, :cnt], np.sort(ref[:cnt])), f"row {t}"
+        assert (out[t, cnt:] == -1).all(), f"row {t}"
 
 
 @pytest.mark.parametrize("n", [1, 8, 9, 16383, 16384, 16385, 16392, 100003, 1 << 20])

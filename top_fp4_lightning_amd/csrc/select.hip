@@ -12,8 +12,8 @@
 //
 // The winners are written in ascending position order (the natural order for gathering the
 // selected keys afterwards), with no sort on the hot paths:
-//  - rows of at most 16384 values: one 1024-thread block per row, 16 composites per thread in
-//    registers (one launch); the first radix pass runs over the whole row, the remaining ones on
+//  - rows of at most 16384 values: one block per row (256, 512 or 1024 threads by row capacity),
+//    16 composites per thread in registers (one launch); the first radix pass runs over the whole row, the remaining ones on
 //    the elements of the threshold digit only (copied to LDS, one wavefront, no block barriers);
 //    winners are compacted in slot order with wavefront ballots, which is
 //    position order when the optional block map is ascending (as the pool and this function
@@ -338,9 +338,11 @@ __device__ __forceinline__ void write_pad(const SelectArgs& a, int64_t t, uint32
 }
 
 // ---------------------------------------------------------------- rows of <= 16384 values
-constexpr int kRowThreads = 1024;
-constexpr int kRowPer = kSmallRow / kRowThreads;  // 16 composites per thread, in registers
-constexpr int kListCap = 4096;                    // LDS candidates for the wave-level passes
+// One block per row, 16 composites per thread in registers; the block size follows the row
+// capacity (256 threads up to 4096 values, 512 up to 8192, 1024 up to 16384) so that many short
+// rows keep many blocks resident.
+constexpr int kRowPer = 16;
+constexpr int kListMax = 4096;  // LDS candidates for the wave-level passes
 
 // Radix passes p0..5 by one wavefront over a candidate list in LDS (no block barriers); same
 // contract as radix_pass. h is a padded 2048-bin histogram owned by this wave.
@@ -367,29 +369,32 @@ __device__ uint64_t wave_radix(const uint64_t* list, uint32_t n, uint32_t need, 
     return prefix;
 }
 
-__global__ __launch_bounds__(kRowThreads) void select_small_kernel(SelectArgs a) {
-    constexpr int NW = kRowThreads / 64;
-    __shared__ Hist<kRowThreads> H;
+template <int NT>
+__global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
+    constexpr int NW = NT / 64;
+    constexpr int Q = kRowPer * NW / 64;  // (slot, wave) counts per lane in the compaction scan
+    static_assert(Q >= 1 && kRowPer * NW % 64 == 0, "compaction scan needs a whole number of counts per lane");
+    __shared__ Hist<NT> H;
     __shared__ Sel sel;
     __shared__ uint32_t woff[kRowPer][NW];
     __shared__ uint32_t cnt_all;
     __shared__ uint32_t seg_cnt[NW];
     __shared__ uint64_t T_sh;
     // the candidate list reuses the per-wave histogram words, dead after the first pass
-    static_assert(sizeof(H.hw) >= kListCap * sizeof(uint64_t), "candidate list must fit in the histogram space");
+    constexpr int kListCap = sizeof(H.hw) / sizeof(uint64_t) < kListMax ? sizeof(H.hw) / sizeof(uint64_t) : kListMax;
     uint64_t* list = reinterpret_cast<uint64_t*>(&H.hw[0][0]);
     const int64_t t = blockIdx.x;
     const RowInfo ri = row_info(a, t);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     uint64_t c[kRowPer];
-    load_composites<kRowPer>(a, t, ri, threadIdx.x, kRowThreads, c);
+    load_composites<kRowPer>(a, t, ri, threadIdx.x, NT, c);
     auto each = [&](auto&& f) {
 #pragma unroll
         for (int j = 0; j < kRowPer; ++j) f(c[j]);
     };
     uint32_t need = (uint32_t)a.k;
     uint64_t prefix = 0ull, mask = 0ull, T = ~0ull;
-    if (ri.len > 0 && !radix_pass<kRowThreads>(each, 0, need, prefix, mask, T, H, sel)) {
+    if (ri.len > 0 && !radix_pass<NT>(each, 0, need, prefix, mask, T, H, sel)) {
         // the threshold digit holds H.h[d] candidates; when they fit, they are packed into one LDS
         // list (per-wave offsets from ballot counts, no atomics) and one wavefront finishes on them
         const uint32_t ncand = H.h[hidx(sel.digit)];
@@ -420,7 +425,7 @@ __global__ __launch_bounds__(kRowThreads) void select_small_kernel(SelectArgs a)
             T = T_sh;
         } else {
             for (int p = 1; p < 6; ++p)
-                if (radix_pass<kRowThreads>(each, p, need, prefix, mask, T, H, sel)) break;
+                if (radix_pass<NT>(each, p, need, prefix, mask, T, H, sel)) break;
         }
     }
     // ordered compaction: slot order (j, wave, lane)
@@ -431,11 +436,11 @@ __global__ __launch_bounds__(kRowThreads) void select_small_kernel(SelectArgs a)
         if (lane == 0) woff[j][w] = (uint32_t)__popcll(m[j]);
     }
     __syncthreads();
-    if (threadIdx.x < 64) {  // exclusive scan of the kRowPer * NW (j, wave) counts, 4 per lane
-        uint32_t e[4], s = 0;
+    if (threadIdx.x < 64) {  // exclusive scan of the kRowPer * NW (j, wave) counts, Q per lane
+        uint32_t e[Q], s = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int idx = 4 * lane + q;
+        for (int q = 0; q < Q; ++q) {
+            const int idx = Q * lane + q;
             e[q] = woff[idx / NW][idx % NW];
             s += e[q];
         }
@@ -447,8 +452,8 @@ __global__ __launch_bounds__(kRowThreads) void select_small_kernel(SelectArgs a)
         }
         uint32_t run = u - s;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int idx = 4 * lane + q;
+        for (int q = 0; q < Q; ++q) {
+            const int idx = Q * lane + q;
             woff[idx / NW][idx % NW] = run;
             run += e[q];
         }
@@ -676,7 +681,13 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
     if (a.nq <= 0) return hipSuccess;
     const int64_t cap = row_cap(a);
     if (cap <= kSmallRow) {
-        hipLaunchKernelGGL(select_small_kernel, dim3((unsigned)a.nq), dim3(kRowThreads), 0, stream, a);
+        const dim3 grid((unsigned)a.nq);
+        if (cap <= 256 * kRowPer)
+            hipLaunchKernelGGL(select_small_kernel<256>, grid, dim3(256), 0, stream, a);
+        else if (cap <= 512 * kRowPer)
+            hipLaunchKernelGGL(select_small_kernel<512>, grid, dim3(512), 0, stream, a);
+        else
+            hipLaunchKernelGGL(select_small_kernel<1024>, grid, dim3(1024), 0, stream, a);
         return hipGetLastError();
     }
     const WsView v = ws_view(a.ws, a.nq, cap);
