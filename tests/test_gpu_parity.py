@@ -295,22 +295,36 @@ def test_topk_with_block_map(fx, nblocks, k):
         assert (out[t, cnt:] == -1).all()
 
 
-@pytest.mark.parametrize("n_keys,nqs,group", [(6000, 48, 48), (3000, 37, 37), (20000, 70, 35)])
-def test_multi_query_scan_matches_single_query(fx, pl, n_keys, nqs, group):
-    # the many-query scan (group > 1) must reproduce the per-query scan bit for bit
+@pytest.mark.parametrize("outputs", ["both", "block_max", "scores"])
+@pytest.mark.parametrize("n_keys,nqs,group", [(6000, 48, 48), (3000, 37, 37), (20000, 70, 35), (9000, 16, 16)])
+def test_multi_query_scan_matches_single_query(fx, pl, n_keys, nqs, group, outputs):
+    # the many-query scan (group > 1) must reproduce the per-query scan bit for bit, for each
+    # combination of requested outputs (untouched entries stay NaN on both sides)
     wl = synth.prefill_workload("mq", 205 + nqs, n_keys, nqs)
     dev = pl.DeviceWorkload.from_workload(wl, group=group)
     if group < nqs:  # two groups over the same keys, the second with its own causal bounds
         dev.n_vis = torch.cat([dev.n_vis[:group], dev.n_vis[:group] - 1000])
     qc, qs = fx.idx_quantize_q(dev.q[0], dev.signs)
     nb = (dev.max_n + 7) // 8
+    want_sc = outputs in ("both", "scores")
+    want_bm = outputs in ("both", "block_max")
     outs = []
     for g in (1, group):
         sc = torch.full((wl.nq, dev.max_n), float("nan"), device="cuda")
         bm = torch.full((wl.nq, nb), float("nan"), device="cuda")
         fx.idx_score_full(dev.k_codes, dev.k_scales, dev.k_base, dev.n_vis, qc, qs, dev.w[0], dev.max_n, group=g,
-                          scores=sc, block_max=bm)
+                          scores=sc if (g == 1 or want_sc) else None, block_max=bm if (g == 1 or want_bm) else None)
         outs.append((sc, bm))
     torch.cuda.synchronize()
-    assert torch.equal(torch.nan_to_num(outs[0][0], nan=7.0), torch.nan_to_num(outs[1][0], nan=7.0))
-    assert torch.equal(torch.nan_to_num(outs[0][1], nan=7.0), torch.nan_to_num(outs[1][1], nan=7.0))
+    if want_sc:
+        assert torch.equal(torch.nan_to_num(outs[0][0], nan=7.0), torch.nan_to_num(outs[1][0], nan=7.0))
+    if want_bm:
+        assert torch.equal(torch.nan_to_num(outs[0][1], nan=7.0), torch.nan_to_num(outs[1][1], nan=7.0))
+    # nothing beyond a query's visible blocks is written
+    nvis = dev.n_vis.cpu().numpy()
+    for t in range(wl.nq):
+        nbt = (int(nvis[t]) + 7) // 8
+        if want_bm:
+            assert torch.isnan(outs[1][1][t, nbt:]).all(), f"block max written past query {t}"
+        if want_sc:
+            assert torch.isnan(outs[1][0][t, int(nvis[t]):]).all(), f"score written past query {t}"

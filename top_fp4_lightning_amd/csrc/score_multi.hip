@@ -10,6 +10,9 @@ namespace {
 #ifndef FP4IDX_MULTI_WAVES
 #define FP4IDX_MULTI_WAVES 1
 #endif
+#ifndef FP4IDX_MULTI_ORDER
+#define FP4IDX_MULTI_ORDER 0
+#endif
 // Many queries sharing one key range (chunked prefill, speculative decode).
 //
 // Work unit: a tile of 32 keys against all 32 heads of one query as two
@@ -98,18 +101,23 @@ __device__ __forceinline__ float combine2(float p0, float p1) {
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// Keys of one 64-key step are staged in LDS once per block: 4 KiB of codes (16-byte chunks
-// XOR-swizzled so that eight consecutive keys fall on distinct bank groups, both for the
-// staging writes and the operand reads) and 256 bytes of scales. Two buffers alternate; one
-// barrier per step orders the writes of step s + 1 before its reads and the reads of step s - 1
-// before the buffer is overwritten. Control flow around the barriers is uniform per block.
+// Keys are staged in LDS once per block, two 64-key steps at a time: per step 4 KiB of codes
+// (16-byte chunks XOR-swizzled so that eight consecutive keys fall on distinct bank groups, both
+// for the staging writes and the operand reads) and 256 bytes of scales. Two buffers alternate;
+// one barrier per staged block orders the writes of block s + 1 before its reads and the reads
+// of block s - 1 before the buffer is overwritten. Control flow around the barriers is uniform
+// per block.
+//
+// Block maxima: after a step, all eight lanes of a key block hold its maximum; lane 8g + s keeps
+// block g of step s (mod 8) in one register per query, and every eighth step (or at the wave's
+// last step) the wave writes the 64 maxima of those 8 steps with one 256-byte store.
 constexpr int kStepKeys = 64;
+constexpr int kStageSteps = 2;                      // 64-key steps per staged block (one barrier)
 constexpr int kStageCodes = kStepKeys * kRowBytes;  // bytes of codes per step
-constexpr int kStageScales = kStepKeys * kGroups;
 
 struct StageBuf {
-    alignas(16) uint8_t codes[2][kStageCodes];
-    alignas(16) uint32_t scales[2][kStepKeys];
+    alignas(16) uint8_t codes[2][kStageSteps][kStageCodes];
+    alignas(16) uint32_t scales[2][kStageSteps * kStepKeys];
 };
 
 // LDS byte offset of 16-byte chunk p (0..3) of key kk (0..63) of a step
@@ -169,78 +177,104 @@ __global__ __launch_bounds__(256, FP4IDX_MULTI_WAVES) void score_multi_kernel(Sc
         brow[i] = BMAX ? a.block_max + qq * a.bm_stride : nullptr;
     }
 
-    // staging: thread T carries 16-byte chunk T % 4 of key T / 4; wave 0 also the scale words
+    // staging: for every step of a staged block, thread T carries 16-byte chunk T % 4 of key
+    // T / 4; threads below 128 also carry one scale word
     const int T = threadIdx.x;
     const uint32_t st_code = stage_chunk(T >> 2, T & 3);
-    v4i st_c;
+    v4i st_c[kStageSteps];
     uint32_t st_s = 0;
-    auto stage_load = [&](int e0) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(kr.codes, (uint32_t)e0 * kRowBytes + (uint32_t)T * 16u, 0,
-                                                            kReuse);
-        st_c = v4i{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
-        if (wave == 0)
-            st_s = __builtin_amdgcn_raw_buffer_load_b32(kr.scales, (uint32_t)(e0 + T) * kGroups, 0, kReuse);
+    auto stage_load = [&](int sg) {
+        const uint32_t e0 = (uint32_t)(e_begin + sg * kStageSteps * kStepKeys);
+#pragma unroll
+        for (int ss = 0; ss < kStageSteps; ++ss) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+                kr.codes, (e0 + ss * kStepKeys) * kRowBytes + (uint32_t)T * 16u, 0, kReuse);
+            st_c[ss] = v4i{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+        }
+        if (T < kStageSteps * kStepKeys)
+            st_s = __builtin_amdgcn_raw_buffer_load_b32(kr.scales, (e0 + (uint32_t)T) * kGroups, 0, kReuse);
     };
     auto stage_store = [&](int buf) {
-        *reinterpret_cast<v4i*>(__builtin_assume_aligned(&sb.codes[buf][st_code], 16)) = st_c;
-        if (wave == 0) sb.scales[buf][T] = st_s;
+#pragma unroll
+        for (int ss = 0; ss < kStageSteps; ++ss)
+            *reinterpret_cast<v4i*>(__builtin_assume_aligned(&sb.codes[buf][ss][st_code], 16)) = st_c[ss];
+        if (T < kStageSteps * kStepKeys) sb.scales[buf][T] = st_s;
     };
-    // operands of tile u (keys 32u .. 32u + 31 of the step) from buffer buf
-    auto read_tiles = [&](int buf, KTile32 (&t)[2]) {
+    // operands of tile u (keys 32u .. 32u + 31) of step ss of buffer buf
+    auto read_tiles = [&](int buf, int ss, KTile32 (&t)[2]) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int kk = 32 * u + c;
 #pragma unroll
             for (int k = 0; k < 2; ++k)
                 t[u].b[k] = *reinterpret_cast<const v4i*>(
-                    __builtin_assume_aligned(&sb.codes[buf][stage_chunk(kk, 2 * h + k)], 16));
-            t[u].sc = (int)reinterpret_cast<const uint16_t*>(&sb.scales[buf][kk])[h];
+                    __builtin_assume_aligned(&sb.codes[buf][ss][stage_chunk(kk, 2 * h + k)], 16));
+            t[u].sc = (int)reinterpret_cast<const uint16_t*>(&sb.scales[buf][ss * kStepKeys + kk])[h];
         }
     };
 
-    // score one 64-key step for every query; MASKED steps drop keys past each query's count
-    auto step = [&](const KTile32 (&t)[2], int e0, auto masked) {
+    // the wave scores steps 0 .. last (its queries see keys below nmax)
+    const int last = (nmax - e_begin + kStepKeys - 1) / kStepKeys < n_steps
+                         ? (nmax - e_begin + kStepKeys - 1) / kStepKeys - 1
+                         : n_steps - 1;
+    float bacc[QW];
+#pragma unroll
+    for (int i = 0; i < QW; ++i) bacc[i] = -INFINITY;
+
+    // score step `it` for every query; MASKED steps drop keys past each query's count
+    auto step = [&](const KTile32 (&t)[2], int it, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
+        const int e0 = e_begin + it * kStepKeys;
         const int el = e0 + lane;
+        const bool flush = (it & 7) == 7 || it == last;  // uniform
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
             const v16f o0 = mfma_tile32(q[i], t[0]);
             const v16f o1 = mfma_tile32(q[i], t[1]);
+#if FP4IDX_MULTI_ORDER == 1
+            __builtin_amdgcn_sched_barrier(0);
+#endif
             const float sc = combine2(lane_partial32(q[i], o0), lane_partial32(q[i], o1));
-            if (!MASKED) {
-                if (SCORES) srow[i][el] = sc;
-                // all eight lanes of a block hold its maximum and store the same value
-                if (BMAX) brow[i][el >> 3] = max8(sc);
-            } else {
-                const bool valid = el < nq_[i];
-                if (SCORES && valid) srow[i][el] = sc;
-                if (BMAX) {
-                    const float m = max8(valid ? sc : -INFINITY);
-                    if (valid) brow[i][el >> 3] = m;
+            const bool valid = !MASKED || el < nq_[i];
+            if (SCORES && valid) srow[i][el] = sc;
+            if (BMAX) {
+                const float m = max8(valid ? sc : -INFINITY);
+                bacc[i] = (lane & 7) == (it & 7) ? m : bacc[i];
+                if (flush) {
+                    // lane 8g + s holds block g of step (it & ~7) + s
+                    const int s_ = lane & 7, g_ = lane >> 3;
+                    const int blk = (e_begin >> 3) + (it & ~7) * 8 + s_ * 8 + g_;
+                    if (s_ <= (it & 7) && blk < (nq_[i] + kBlock - 1) / kBlock) brow[i][blk] = bacc[i];
                 }
             }
             // one query's matrix results live at a time: keeps the wave within the register
             // budget of four waves per SIMD (other waves hide the matrix latency)
+#if FP4IDX_MULTI_ORDER != 2
             __builtin_amdgcn_sched_barrier(0);
+#endif
         }
     };
 
-    stage_load(e_begin);
+    const int n_stages = (n_steps + kStageSteps - 1) / kStageSteps;
+    stage_load(0);
     stage_store(0);
-    if (n_steps > 1) stage_load(e_begin + kStepKeys);
+    if (n_stages > 1) stage_load(1);
     __syncthreads();
-    for (int it = 0; it < n_steps; ++it) {
-        const int e0 = e_begin + it * kStepKeys;
-        if (e0 < nmax) {  // uniform per wave
-            KTile32 t[2];
-            read_tiles(it & 1, t);
-            if (e0 + kStepKeys <= nmin)
-                step(t, e0, std::false_type{});
-            else
-                step(t, e0, std::true_type{});
+    for (int sg = 0; sg < n_stages; ++sg) {
+#pragma unroll
+        for (int ss = 0; ss < kStageSteps; ++ss) {
+            const int it = sg * kStageSteps + ss;
+            if (it <= last) {  // uniform per wave
+                KTile32 t[2];
+                read_tiles(sg & 1, ss, t);
+                if (e_begin + (it + 1) * kStepKeys <= nmin)
+                    step(t, it, std::false_type{});
+                else
+                    step(t, it, std::true_type{});
+            }
         }
-        if (it + 1 < n_steps) stage_store((it + 1) & 1);
-        if (it + 2 < n_steps) stage_load(e0 + 2 * kStepKeys);
+        if (sg + 1 < n_stages) stage_store((sg + 1) & 1);
+        if (sg + 2 < n_stages) stage_load(sg + 2);
         __syncthreads();
     }
 }
