@@ -57,8 +57,8 @@ def measured_traffic(record: str) -> int | None:
 
 def cpu_baseline(wl, max_queries: int = 8) -> dict:
     """The oracle (plain C, threaded over queries) on a bounded sample: the Full layer of the
-    first min(8, cores) sequences of the same workload (score every key, top-512, block maxima,
-    pin, pool). The oracle quantises its own keys first (untimed)."""
+    first min(8, cores) queries of the same workload (score every visible key, top-512, block
+    maxima, pin, pool). The oracle quantises the keys of their sequences first (untimed)."""
     import numpy as np
 
     import oracle
@@ -66,18 +66,21 @@ def cpu_baseline(wl, max_queries: int = 8) -> dict:
     cores = os.cpu_count() or 1
     nqs = max(1, min(max_queries, wl.nq, cores))
     s = wl.signs()
-    log(f"cpu baseline: oracle quantises {nqs} x {int(wl.seq_len[0])} keys (untimed)")
-    kcs, kss = [], []
-    for b in range(nqs):
+    seqs = sorted(set(int(b) for b in wl.qseq[:nqs]))
+    log(f"cpu baseline: oracle quantises the keys of {len(seqs)} sequence(s) (untimed)")
+    kcs, kss, seq_off, off = [], [], {}, 0
+    for b in seqs:
         kc, ks = oracle.quantize(wl.keys(b), s, nthreads=cores)
         kcs.append(kc)
         kss.append(ks)
+        seq_off[b] = off
+        off += kc.shape[0]
     kc = np.concatenate(kcs)
     ks = np.concatenate(kss)
     qc, qs = oracle.quantize(wl.q(0, range(nqs)), s)
     w = wl.w(0, range(nqs))
     n = wl.n_vis[:nqs].astype(np.int64)
-    base = np.concatenate([[0], np.cumsum(n)[:-1]]).astype(np.int64)
+    base = np.array([seq_off[int(b)] for b in wl.qseq[:nqs]], dtype=np.int64)
     log(f"cpu baseline: timing the oracle Full layer on {nqs} queries with {nqs} threads")
     t0 = time.perf_counter()
     oracle.decode_batch(kc, ks, base, n, qc, qs, w, k=wl.k, nthreads=nqs)
@@ -85,7 +88,7 @@ def cpu_baseline(wl, max_queries: int = 8) -> dict:
     entries = int(n.sum())
     return {"value": entries / dt, "unit": "entries/s", "cores": nqs, "kind": "oracle",
             "sample": f"Full layer (score all keys, top-512, block max, pin, top-2048 pool) of {nqs} of the "
-                      f"{wl.nq} sequences x {int(n[0])} keys; {dt:.2f} s wall on {nqs} threads",
+                      f"{wl.nq} queries x {int(n[0])} keys; {dt:.2f} s wall on {nqs} threads",
             "seconds": round(dt, 3)}
 
 
@@ -135,41 +138,24 @@ def bench_prefill(wl, args) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="fullscan_1m")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="only copy 512 MiB device-to-device 5 times (calibrates the HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the indexer shards by "
-              "sequence with no exchange, or by key range with one all-gather of per-shard candidates)",
-              file=sys.stderr)
-        return 2
+DECODE_CONFIGS = {
+    "fullscan_1m": "fullscan_1m decode step: batch 8 x 1048576 keys (m=1), Full scan + top-512 + "
+                   "pool(2048 blocks of 8) + 4 Reindex layers",
+    "spec_decode_1m": "spec_decode_1m verify step: batch 8 x 1048576 keys (m=1), 6 positions per sequence "
+                      "(token + 5 draft), Full scan + top-512 + pool(2048 blocks of 8) + 4 Reindex layers",
+}
 
+
+def bench_decode(wl, args) -> int:
+    """One decode step per timed iteration (quantise, Full scan, pool, Full top-512 through the
+    pool, Reindex layers). With one query per sequence the Full scan is the single-query kernel
+    and the roofline is HBM; with several positions per sequence (speculative verification) it is
+    the many-query kernel and the roofline is FP4 MFMA."""
     import numpy as np
     import torch
 
-    import synth
-    import top_fp4_lightning_amd as fx
     from top_fp4_lightning_amd import pipeline
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.copy_probe:
-        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": src.numel(), "launches": 5}), flush=True)
-        return 0
-    wl = synth.config(args.workload)
-    if args.workload == "prefill_128k":
-        return bench_prefill(wl, args)
     t = time.perf_counter()
     dev = pipeline.DeviceWorkload.from_workload(wl)
     torch.cuda.synchronize()
@@ -208,8 +194,24 @@ def main() -> int:
     pool_pos = int(sum(min(n, 8 * min(2048, (n + 7) // 8)) for n in n_vis))
     entries = int(sum(n_vis)) + plan.layers * pool_pos
     queries = wl.nq * (1 + plan.layers)
-    sb = scan_bytes(n_vis, wl.nq)
-    achieved = sb / (scan_ms / 1000.0) / 1e9
+    if dev.group == 1:
+        sb = scan_bytes(n_vis, wl.nq)
+        achieved = sb / (scan_ms / 1000.0) / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS,
+                    "traffic": measured_traffic("score_full_fullscan_1m_traffic") if wl.name == "fullscan_1m" else None,
+                    "kernel": "score_full_kernel", "algorithmic_bytes_per_launch": sb}
+    else:
+        # many-query scan: keys are read once per group, the matrix work grows with the positions
+        flop = 2.0 * 4096.0 * float(sum(n_vis))
+        groups = [n_vis[i:i + dev.group] for i in range(0, len(n_vis), dev.group)]
+        sb = sum(max(g) * 68 for g in groups) + wl.nq * (32 * 68 + 32 * 4) + sum((n + 7) // 8 for n in n_vis) * 4
+        achieved = flop / (scan_ms / 1000.0) / 1e12
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / MFMA_FP4_PEAK_TFLOPS, "traffic": None, "kernel": "score_multi_kernel",
+                    "algorithmic_flop_per_launch": flop, "algorithmic_bytes_per_launch": sb,
+                    "hbm_achieved_gbs": sb / (scan_ms / 1000.0) / 1e9,
+                    "hbm_frac": sb / (scan_ms / 1000.0) / 1e9 / HBM_PEAK_GBS}
     res = {
         "metric": "indexer entries scored/s + top-512 queries/s at 1M ctx; % of HBM roofline",
         "value": entries / (ms_step / 1000.0),
@@ -223,22 +225,56 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "mxfp4",
         "data": "synthetic (seeded N(0,1) bf16 q/k, N(0,1/32) w, 1% planted keys; no trained weights)",
-        "config": {"workload": "fullscan_1m decode step: batch 8 x 1048576 keys (m=1), Full scan + top-512 + "
-                               "pool(2048 blocks of 8) + 4 Reindex layers",
-                   "batch": wl.nq, "context": n_vis[0], "reindex_layers": plan.layers, "k": 512,
-                   "pool_blocks": 2048, "block": 8},
+        "config": {"workload": DECODE_CONFIGS.get(wl.name, wl.name),
+                   "batch": wl.nseq, "positions_per_sequence": dev.group, "context": int(wl.seq_len[0]),
+                   "reindex_layers": plan.layers, "k": 512, "pool_blocks": 2048, "block": 8},
         "top512_queries_per_s": queries / (ms_step / 1000.0),
         "full_scan_entries_per_s": int(sum(n_vis)) / (scan_ms / 1000.0),
         "scan_ms": scan_ms,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("score_full_fullscan_1m_traffic"),
-                     "kernel": "score_full_kernel", "algorithmic_bytes_per_launch": sb},
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)
     return 0
 
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="fullscan_1m")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only copy 512 MiB device-to-device 5 times (calibrates the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the indexer shards by "
+              "sequence with no exchange, or by key range with one all-gather of per-shard candidates)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    import top_fp4_lightning_amd as fx
+    from top_fp4_lightning_amd import pipeline
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": src.numel(), "launches": 5}), flush=True)
+        return 0
+    wl = synth.config(args.workload)
+    if args.workload == "prefill_128k":
+        return bench_prefill(wl, args)
+    return bench_decode(wl, args)
 
 if __name__ == "__main__":
     sys.exit(main())

@@ -16,8 +16,9 @@
  * Data layout shared by every entry point ("indexer rows"):
  *  - an indexer row is one 128-dim vector (a query head or a key) in MXFP4: 64 code bytes, two
  *    E2M1 codes per byte with element 2i in the low nibble of byte i, plus 4 UE8M0 scale bytes,
- *    one per group of 32 elements (byte value = exponent + 127) ([P1] "the scale format decides
- *    precision": groups of 32 with an E8M0 scale, 4.25 bits per element, 68 bytes per key);
+ *    one per group of 32 elements (byte value = exponent + 127, 0 .. 254; 255, the E8M0 NaN, is
+ *    outside the contract) ([P1] "the scale format decides precision": groups of 32 with an E8M0
+ *    scale, 4.25 bits per element, 68 bytes per key);
  *  - codes live in one array [rows][64] and scales in another [rows][4];
  *  - a query is 32 consecutive rows (heads 0..31), weights are fp32 [nq][32].
  */

@@ -145,6 +145,7 @@ class Workload:
     k: int = 512
     block: int = 8
     topk_blocks: int = 2048
+    group: int = 1  # consecutive queries that share one sequence's key range
 
     @property
     def nseq(self) -> int:
@@ -227,7 +228,20 @@ def prefill_workload(name: str, seed: int, n_keys: int, n_queries: int, k: int =
     return Workload(name=name, seed=seed, seq_len=np.array([n_keys], dtype=np.int64),
                     qseq=np.zeros(n_queries, dtype=np.int64),
                     n_vis=np.arange(first, first + n_queries, dtype=np.int64), layers=0,
-                    plant_query=np.array([min(tp, n_queries - 1)], dtype=np.int64), k=k)
+                    plant_query=np.array([min(tp, n_queries - 1)], dtype=np.int64), k=k, group=n_queries)
+
+
+def spec_decode_workload(name: str, seed: int, seq_len, positions: int = 6, layers: int = 0,
+                         k: int = 512) -> Workload:
+    """Speculative verification: `positions` consecutive queries per sequence (the token plus the
+    draft positions), query j of a sequence of n entries seeing positions <= n - positions + j.
+    The sequence's first query plants its keys."""
+    seq_len = np.asarray(seq_len, dtype=np.int64)
+    nseq = len(seq_len)
+    qseq = np.repeat(np.arange(nseq, dtype=np.int64), positions)
+    n_vis = np.repeat(seq_len, positions) - positions + 1 + np.tile(np.arange(positions, dtype=np.int64), nseq)
+    return Workload(name=name, seed=seed, seq_len=seq_len, qseq=qseq, n_vis=n_vis, layers=layers,
+                    plant_query=np.arange(nseq, dtype=np.int64) * positions, k=k, group=positions)
 
 
 # The five workloads the indexer is measured on (sizes from the problem statement).
@@ -244,7 +258,10 @@ def config(name: str) -> Workload:
         return decode_workload(name, 4, [1 << 19] * 8)
     if name == "prefill_128k":  # 4096 queries on 131072 keys, causal
         return prefill_workload(name, 5, 131072, 4096)
+    if name == "spec_decode_1m":  # 8 x 2^20, the token + 5 draft positions per sequence, 4 Reindex layers
+        return spec_decode_workload(name, 6, [1 << 20] * 8, positions=6, layers=4)
     raise KeyError(name)
 
 
-CONFIGS = ("decode_32k", "decode_batch64", "reindex_1m", "fullscan_1m", "fullscan_512k", "prefill_128k")
+CONFIGS = ("decode_32k", "decode_batch64", "reindex_1m", "fullscan_1m", "fullscan_512k", "prefill_128k",
+           "spec_decode_1m")

@@ -127,6 +127,14 @@ def test_reindex_1m(pl):
     check_decode_queries(wl, out, sample=[0, 63])
 
 
+def test_spec_decode_1m(pl):
+    # 8 x 2^20 keys, 6 positions per sequence (the token + 5 draft positions) scanned together by
+    # the many-query kernel; pool, Full top-512 and 4 Reindex layers per position
+    wl = synth.config("spec_decode_1m")
+    out = run_decode(pl, wl)
+    check_decode_queries(wl, out, sample=[0, 5, 46])
+
+
 def test_prefill_128k(pl):
     # 4096 queries on 131072 keys, query i sees positions <= 126976 + i
     wl = synth.config("prefill_128k")

@@ -47,3 +47,15 @@ def test_configs_shapes():
     assert c5.nq == 4096 and c5.n_vis[0] == 126977 and c5.n_vis[-1] == 131072
     c4 = synth.config("fullscan_1m")
     assert c4.nq == 8 and (c4.n_vis == 1 << 20).all()
+    assert c5.group == 4096 and c4.group == 1
+
+
+def test_spec_decode_shape():
+    # the token plus 5 draft positions per sequence: 6 consecutive queries sharing the sequence's
+    # keys, position j of a sequence of n entries seeing n - 5 + j of them
+    w = synth.config("spec_decode_1m")
+    assert w.nseq == 8 and w.nq == 48 and w.group == 6 and w.layers == 4
+    assert np.array_equal(w.qseq, np.repeat(np.arange(8), 6))
+    assert np.array_equal(w.n_vis[:6], (1 << 20) - 5 + np.arange(6))
+    assert (w.k_base[6:12] == 1 << 20).all() and (w.k_base[:6] == 0).all()
+    assert np.array_equal(w.plant_query, np.arange(8) * 6)

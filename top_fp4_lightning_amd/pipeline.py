@@ -11,6 +11,10 @@ scoring"):
      the pool, and a pooled key's score is computed by the same per-key arithmetic.
   5. for each Reindex layer: idx_quantize_q, idx_score_pool_gather, idx_topk -> its top-512.
 
+Several queries per sequence (speculative verification of the draft positions, "DeepSeek-V4.1-Flash
+inference-side full breakdown", section 8.2): the same decode step with group = positions per
+sequence, so the Full scan reads each key once for all of them (the many-query scan).
+
 Prefill (a chunk of queries sharing one key range, causal): idx_score_full writes block maxima
 for every query; idx_topk keeps the 512 best blocks per query (a top-512 key's block is among
 them); idx_score_pool_gather re-scores those 4096 keys; idx_topk takes the final 512.
@@ -48,8 +52,10 @@ class DeviceWorkload:
         return int(self.n_vis.shape[0])
 
     @staticmethod
-    def from_workload(wl, device="cuda", chunk_rows: int = 1 << 20, group: int = 1) -> "DeviceWorkload":
-        """Generate a seeded workload's keys on the host in chunks and quantise them on the GPU."""
+    def from_workload(wl, device="cuda", chunk_rows: int = 1 << 20, group: int | None = None) -> "DeviceWorkload":
+        """Generate a seeded workload's keys on the host in chunks and quantise them on the GPU.
+        `group` (default: the workload's) is the run of consecutive queries sharing a key range."""
+        group = wl.group if group is None else group
         signs = torch.from_numpy(wl.signs()).to(device)
         total = wl.total_keys
         k_codes = torch.empty(total, 64, dtype=torch.uint8, device=device)
@@ -103,7 +109,7 @@ class DecodePlan:
     def full_scan(self, stream=None):
         dv = self.dev
         idx_score_full(dv.k_codes, dv.k_scales, dv.k_base, dv.n_vis, self.q_codes[0], self.q_scales[0], dv.w[0],
-                       dv.max_n, group=1, scores=self.scores, block_max=self.block_max, stream=stream)
+                       dv.max_n, group=dv.group, scores=self.scores, block_max=self.block_max, stream=stream)
 
     def build_pool(self, stream=None):
         idx_build_pool(self.block_max, self.dev.n_vis, self.dev.max_n, self.pool_blocks, self.pool_count,
