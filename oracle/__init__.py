@@ -33,7 +33,8 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        src = os.path.join(_HERE, "oracle.c")
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(src) > os.path.getmtime(_LIB_PATH):
             build()
         L = ctypes.CDLL(_LIB_PATH)
         P, i64, i32, d = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
@@ -58,6 +59,15 @@ def lib():
         L.orc_block_max.restype = i64
         L.orc_pool.argtypes = [P, i64, i32, i32, P]
         L.orc_pool.restype = i32
+        L.orc_e4m3_value.argtypes = [ctypes.c_int]
+        L.orc_e4m3_value.restype = d
+        L.orc_e4m3_scale_for.argtypes = [d]
+        L.orc_e4m3_scale_for.restype = ctypes.c_int
+        L.orc_mkv_quantize_rows.argtypes = [P, i64, P, P]
+        L.orc_mkv_value.argtypes = [P, P, ctypes.c_int]
+        L.orc_mkv_value.restype = d
+        L.orc_mkv_gather.argtypes = [P, P, P, P, P, i32, i32, i64, P]
+        L.orc_mkv_gather.restype = i64
         L.orc_reindex_mask.argtypes = [P, i64, P, i32, i32, i32, P]
         L.orc_reindex_mask.restype = i32
         L.orc_reindex_gather.argtypes = [P, P, P, P, P, i64, P, i32, i32, i32, P]
@@ -226,3 +236,51 @@ def mac_count() -> int:
 
 def mac_reset() -> None:
     lib().orc_mac_reset()
+
+
+# ------------------------------------------------------------------ main KV codec
+MKV_DIM = 512
+MKV_GROUP = 16
+
+
+def e4m3_value(b: int) -> float:
+    return lib().orc_e4m3_value(int(b))
+
+
+def e4m3_scale_for(a: float) -> int:
+    return lib().orc_e4m3_scale_for(float(a))
+
+
+def mkv_quantize(x_bf16: np.ndarray):
+    """bf16 bit patterns [rows, 512] -> (codes u8 [rows, 256], E4M3 scales u8 [rows, 32])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16).reshape(-1, MKV_DIM)
+    rows = x.shape[0]
+    codes = np.empty((rows, MKV_DIM // 2), dtype=np.uint8)
+    scales = np.empty((rows, MKV_DIM // MKV_GROUP), dtype=np.uint8)
+    lib().orc_mkv_quantize_rows(_p(x), rows, _p(codes), _p(scales))
+    return codes, scales
+
+
+def mkv_values(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """fp64 values [rows, 512] of stored rows."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1, MKV_DIM // 2)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8).reshape(-1, MKV_DIM // MKV_GROUP)
+    out = np.empty((codes.shape[0], MKV_DIM))
+    for r in range(codes.shape[0]):
+        for c in range(MKV_DIM):
+            out[r, c] = lib().orc_mkv_value(_p(codes[r]), _p(scales[r]), c)
+    return out
+
+
+def mkv_gather(codes, scales, base, n, idx):
+    """bf16 bit patterns [nq, k, 512] of the selected rows (zeros where idx is outside [0, n)),
+    and the count of values that were not exactly representable in bf16."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    base = np.ascontiguousarray(base, dtype=np.int64)
+    n = np.ascontiguousarray(n, dtype=np.int64)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    nq, k = idx.shape
+    out = np.empty((nq, k, MKV_DIM), dtype=np.uint16)
+    bad = lib().orc_mkv_gather(_p(codes), _p(scales), _p(base), _p(n), _p(idx), nq, k, k, _p(out))
+    return out, int(bad)

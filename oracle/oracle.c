@@ -29,6 +29,13 @@
  *    rounds to zero is +0; element 2i is the low nibble of byte i;
  *  - top-k and pool ties go to the lower index; invisible positions never enter a selection.
  *
+ *  - main KV ([P1] "the scale format decides precision" and "removing the global scale"): rows of
+ *    512 values in groups of 16, one E4M3 (OCP "fn": no infinities, S.1111.111 is NaN) scale per
+ *    group and no global scale; the scale is the smallest E4M3 value s with 6 * s >= max|x| of
+ *    the group (the E8M0 rule's "rounded up", on the finer E4M3 grid), saturating at 448; an
+ *    all-zero group gets s = 0 and zero codes; codes as for the indexer rows (nearest, ties to
+ *    even, +0); 256 code bytes + 32 scale bytes per row;
+ *
  * Parity pins (see tests/test_oracle_*.py): E2M1 value set and the rounding thresholds, scale
  * minimality, rotation against a library Hadamard matrix and orthogonality, per-head dot against
  * a dequantised fp64 dot, score special cases, brute-force selection on tiny inputs, the nesting
@@ -441,4 +448,95 @@ void orc_decode_batch(const uint8_t* kc, const uint8_t* ks, const int64_t* base,
     pthread_t th[256];
     for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, decode_worker, &c);
     for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+}
+
+/* ------------------------------------------------------------------ main KV codec
+ * [P1] "the scale format decides precision": 512-value rows, groups of 16 with an E4M3 scale,
+ * no global scale ("removing the global scale still leaves enough range"): 256 + 32 bytes. */
+#define MKV_DIM 512
+#define MKV_GROUP 16
+
+/* value of an E4M3 byte (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 is
+ * subnormal m/8 * 2^-6; S.1111.111 is NaN) */
+double orc_e4m3_value(int b) {
+    const int sgn = (b >> 7) & 1, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+/* byte of the smallest non-negative E4M3 value s with 6 * s >= a (a >= 0): the positive bytes
+ * 0x00 .. 0x7e are in ascending value order; above 6 * 448 the largest (0x7e) */
+int orc_e4m3_scale_for(double a) {
+    for (int b = 0; b <= 0x7e; ++b)
+        if (6.0 * orc_e4m3_value(b) >= a) return b;
+    return 0x7e;
+}
+
+/* one 512-value row of bf16: codes[256] (element 2i in the low nibble of byte i), scales[32] */
+void orc_mkv_quantize_row(const uint16_t* x, uint8_t* codes, uint8_t* scales) {
+    for (int g = 0; g < MKV_DIM / MKV_GROUP; ++g) {
+        double a = 0.0;
+        for (int c = 0; c < MKV_GROUP; ++c) {
+            const double v = fabs(bf16_value(x[g * MKV_GROUP + c]));
+            if (v > a) a = v;
+        }
+        const int b = orc_e4m3_scale_for(a);
+        const double sc = orc_e4m3_value(b);
+        scales[g] = (uint8_t)b;
+        for (int c = 0; c < MKV_GROUP; c += 2) {
+            const int lo = sc > 0.0 ? orc_e2m1_code(bf16_value(x[g * MKV_GROUP + c]) / sc) : 0;
+            const int hi = sc > 0.0 ? orc_e2m1_code(bf16_value(x[g * MKV_GROUP + c + 1]) / sc) : 0;
+            codes[(g * MKV_GROUP + c) / 2] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
+void orc_mkv_quantize_rows(const uint16_t* x, int64_t rows, uint8_t* codes, uint8_t* scales) {
+    for (int64_t r = 0; r < rows; ++r)
+        orc_mkv_quantize_row(x + r * MKV_DIM, codes + r * (MKV_DIM / 2), scales + r * (MKV_DIM / MKV_GROUP));
+}
+
+/* value of element c of a stored row */
+double orc_mkv_value(const uint8_t* codes, const uint8_t* scales, int c) {
+    const int code = (codes[c / 2] >> (4 * (c & 1))) & 15;
+    return orc_e2m1_value(code) * orc_e4m3_value(scales[c / MKV_GROUP]);
+}
+
+/* exact bf16 bit pattern of v; returns 0 and leaves *out untouched when v is not representable */
+static int bf16_exact(double v, uint16_t* out) {
+    const float f = (float)v;
+    if ((double)f != v && !(isnan(v) && isnan(f))) return 0;
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if (!isnan(f) && (u & 0xffffu) != 0) return 0;
+    *out = isnan(f) ? (uint16_t)0x7fc0 : (uint16_t)(u >> 16);
+    return 1;
+}
+
+/* gather-dequantise: out[t][i][0..511] = the bf16 values of row base[t] + idx[t][i] for
+ * 0 <= idx[t][i] < n[t], zeros otherwise. Returns the number of values that were not exactly
+ * representable in bf16 (0 for every E2M1 x E4M3 product). */
+int64_t orc_mkv_gather(const uint8_t* codes, const uint8_t* scales, const int64_t* base, const int64_t* n,
+                       const int32_t* idx, int32_t nq, int32_t k, int64_t idx_stride, uint16_t* out) {
+    int64_t inexact = 0;
+    for (int32_t t = 0; t < nq; ++t)
+        for (int32_t i = 0; i < k; ++i) {
+            const int64_t p = idx[t * idx_stride + i];
+            uint16_t* o = out + ((int64_t)t * k + i) * MKV_DIM;
+            if (p < 0 || p >= n[t]) {
+                memset(o, 0, MKV_DIM * sizeof(uint16_t));
+                continue;
+            }
+            const int64_t r = base[t] + p;
+            for (int c = 0; c < MKV_DIM; ++c)
+                if (!bf16_exact(orc_mkv_value(codes + r * (MKV_DIM / 2), scales + r * (MKV_DIM / MKV_GROUP), c),
+                                &o[c]))
+                    ++inexact;
+        }
+    return inexact;
 }

@@ -22,6 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 
 TAG_SIGNS, TAG_Q, TAG_K, TAG_W, TAG_PLANT, TAG_LEN, TAG_PLANT_Q = 1, 2, 3, 4, 5, 6, 7
+TAG_MKV, TAG_SEL = 40, 41
 NHEAD, DIM = 32, 128
 
 
@@ -42,7 +43,8 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        src = os.path.join(_HERE, "synth.c")
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(src) > os.path.getmtime(_LIB_PATH):
             build()
         L = ctypes.CDLL(_LIB_PATH)
         u64, i64, i32 = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32
@@ -102,6 +104,43 @@ def bf16_rne(x: float) -> int:
 
 def bf16_to_f64(h: np.ndarray) -> np.ndarray:
     return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """round float32 values to bf16 bit patterns, to nearest, ties to even (finite inputs)"""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+MKV_DIM = 512
+
+
+def mkv_rows(seed: int, positions) -> np.ndarray:
+    """Main-KV latent rows (512 values) at arbitrary positions of a seeded cache, as bf16 bit
+    patterns: standard normal values scaled to unit RMS (an RMSNorm with unit weights, the
+    regime the main-KV format is sized for), rounded to bf16."""
+    positions = np.asarray(positions, dtype=np.int64).reshape(-1)
+    out = np.empty((len(positions), MKV_DIM), dtype=np.uint16)
+    for i, p in enumerate(positions):
+        v = normal_f32(seed, TAG_MKV, 0, int(p) * MKV_DIM, MKV_DIM, 1.0).astype(np.float64)
+        v = v / np.sqrt((v * v).mean())
+        out[i] = f32_to_bf16_rne(v.astype(np.float32))
+    return out
+
+
+def selections(seed: int, nq: int, n, k: int) -> np.ndarray:
+    """k distinct ascending positions below n[t] per row t (all of them when n[t] <= k, then -1):
+    stand-ins for a top-k output when only the gather that follows it is measured."""
+    n = np.broadcast_to(np.asarray(n, dtype=np.int64), (nq,))
+    out = np.full((nq, k), -1, dtype=np.int32)
+    for t in range(nq):
+        m = int(n[t])
+        if m <= k:
+            out[t, :m] = np.arange(m)
+            continue
+        rng = np.random.default_rng([seed, TAG_SEL, t])
+        out[t] = np.sort(rng.choice(m, size=k, replace=False)).astype(np.int32)
+    return out
 
 
 def lengths(seed: int, nseq: int, lo: int, span: int) -> np.ndarray:
