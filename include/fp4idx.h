@@ -204,6 +204,47 @@ idx_status idx_topk(const float* scores, int64_t score_stride, const int32_t* n_
                     int32_t k, const int32_t* blocks, int64_t blocks_stride, int32_t block, int32_t* out_idx,
                     int64_t out_stride, float* out_val, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Main-KV FP4 storage ([P1] "the scale format decides precision" and "removing the global scale
+ * still leaves enough range"): a main-KV entry is 512 values stored as E2M1 codes (element 2i in
+ * the low nibble of byte i) with one E4M3 scale per group of 16 values and no global scale,
+ * 256 code bytes + 32 scale bytes = 288 bytes. Codes live in [rows][256], scales in [rows][32].
+ * E4M3 is the OCP FP8 "fn" variant (bias 7, subnormals, no infinities); scale bytes 0x7f and 0xff
+ * (NaN) are outside the contract.
+ */
+
+/*
+ * idx_quantize_kv: write main-KV rows in the storage format.
+ *
+ *   s_g    = the smallest E4M3 value s >= 0 with 6 * s >= max_{c in group g} |x_c| (448 at most);
+ *            the page rounds the ideal max/6 up, as for the indexer's power-of-two scales;
+ *   code_c = E2M1 of x_c / s_g, round to nearest, ties to the even mantissa bit, zero is +0;
+ *            an all-zero group gets s_g = 0 and zero codes.
+ *
+ *   x_bf16 : device, bf16 bit patterns [rows][512], 16-byte aligned, finite values.
+ *   rows   : 0 .. 2^31 (0 enqueues nothing).
+ *   codes  : device uint8 [rows][256], 4-byte aligned (written).
+ *   scales : device uint8 [rows][32] (written).
+ */
+idx_status idx_quantize_kv(const uint16_t* x_bf16, int64_t rows, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * idx_gather_kv: the selected main-KV entries of each query, dequantised to bf16 for core
+ * attention (the cache stores FP4; attention reads dequantised values, [P1] "the scale format
+ * decides precision": the main-KV format is read back before attention, the multiplication does
+ * not happen in 4 bits). Every value is an E2M1 value times an E4M3 scale, exact in bf16.
+ *
+ *   codes, scales : device main-KV cache, [N][256] (4-byte aligned) and [N][32].
+ *   kv_base : device int64 [nq]; position p of query t is cache row kv_base[t] + p.
+ *   n_vis   : device int32 [nq]; positions outside [0, n_vis[t]) (e.g. the -1 padding of
+ *             idx_topk) give rows of zeros.
+ *   nq, k   : queries (at most 65535) and entries per query, nq * k <= 2^31.
+ *   idx     : device int32 [nq][idx_stride] positions (e.g. idx_topk's out_idx), idx_stride >= k.
+ *   out     : device bf16 bit patterns [nq][k][512], 16-byte aligned (written).
+ */
+idx_status idx_gather_kv(const uint8_t* codes, const uint8_t* scales, const int64_t* kv_base, const int32_t* n_vis,
+                         int32_t nq, const int32_t* idx, int64_t idx_stride, int32_t k, uint16_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

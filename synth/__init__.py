@@ -115,6 +115,14 @@ def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
 MKV_DIM = 512
 
 
+def mkv_rows_of(seed: int, seqs, positions) -> np.ndarray:
+    """mkv_rows for (sequence, position) pairs: sequence b's position p is row b * 2^32 + p of
+    one seeded stream, so every sequence has its own rows."""
+    seqs = np.asarray(seqs, dtype=np.int64).reshape(-1)
+    positions = np.asarray(positions, dtype=np.int64).reshape(-1)
+    return mkv_rows(seed, (seqs << 32) + positions)
+
+
 def mkv_rows(seed: int, positions) -> np.ndarray:
     """Main-KV latent rows (512 values) at arbitrary positions of a seeded cache, as bf16 bit
     patterns: standard normal values scaled to unit RMS (an RMSNorm with unit weights, the

@@ -15,9 +15,13 @@ LIB = os.path.join(ROOT, "top_fp4_lightning_amd", "libfp4idx.so")
 @pytest.fixture(scope="module")
 def fx():
     if not os.path.exists(LIB):
-        from top_fp4_lightning_amd.build import build_library
+        import importlib.util
 
-        build_library()
+        spec = importlib.util.spec_from_file_location("fp4idx_build", os.path.join(ROOT, "top_fp4_lightning_amd",
+                                                                                   "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build_library()
     import top_fp4_lightning_amd
 
     return top_fp4_lightning_amd
@@ -32,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["idx_quantize_q", "idx_score_full", "idx_build_pool", "idx_score_pool_gather", "idx_topk",
-              "idx_last_error", "idx_abi_version", "idx_workspace_size"]:
+              "idx_last_error", "idx_abi_version", "idx_workspace_size", "idx_quantize_kv", "idx_gather_kv"]:
         assert n in names
 
 
@@ -138,6 +142,32 @@ def test_gather_and_topk_validation(fx):
     assert t(*bad) == fx.IDX_EINVAL
     bad = list(good); bad[6] = FAKE; bad[7] = 2048; bad[8] = 4
     assert t(*bad) == fx.IDX_EUNSUPPORTED
+
+
+def test_main_kv_validation(fx):
+    q = lambda *a: call(fx, "idx_quantize_kv", *a)
+    assert q(None, 0, None, None, None)[0] == fx.IDX_OK  # empty is a no-op
+    assert q(None, -1, None, None, None)[0] == fx.IDX_EINVAL
+    assert q(FAKE, 3, None, FAKE, None)[0] == fx.IDX_EINVAL
+    assert q(FAKE + 8, 3, FAKE, FAKE, None)[0] == fx.IDX_EALIGN  # bf16 rows are read 16 bytes at a time
+    assert q(FAKE, 3, FAKE + 2, FAKE, None)[0] == fx.IDX_EALIGN
+    g = lambda *a: call(fx, "idx_gather_kv", *a)[0]
+    good = [FAKE, FAKE, FAKE, FAKE, 4, FAKE, 512, 512, FAKE, None]
+    assert g(*[None, None, None, None, 0, None, 0, 0, None, None]) == fx.IDX_OK
+    bad = list(good); bad[5] = None
+    assert g(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[6] = 100  # idx_stride < k
+    assert g(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[8] = FAKE + 8
+    assert g(*bad) == fx.IDX_EALIGN
+    bad = list(good); bad[2] = FAKE + 4  # kv_base is int64
+    assert g(*bad) == fx.IDX_EALIGN
+    bad = list(good); bad[4] = 1 << 30; bad[7] = 8
+    assert g(*bad) == fx.IDX_EUNSUPPORTED
+    bad = list(good); bad[4] = 70000
+    assert g(*bad) == fx.IDX_EUNSUPPORTED
+    bad = list(good); bad[7] = -1
+    assert g(*bad) == fx.IDX_EINVAL
 
 
 def test_python_binding_refuses_cpu_tensors(fx):

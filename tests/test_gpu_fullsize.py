@@ -149,3 +149,19 @@ def test_prefill_128k(pl):
         qc, qs = oracle.quantize(wl.q(0, [t])[0], s)
         I, A = oracle_scores(qc, qs, wl.w(0, [t])[0], kc[:n], ks[:n])
         assert_topk_set(top[t], I, A, 512, f"prefill q{t}")
+
+
+def test_kv_gather_1m(pl):
+    # 64 x 2^20 FP4 main-KV entries in HBM; one selection of 512 per query gathered to bf16;
+    # sampled queries against the oracle's own quantisation and gather of the same rows
+    nseq, n, k, seed = 64, 1 << 20, 512, 12
+    sel = synth.selections(seed, nseq, n, k)
+    plan = pl.MainKVGather(nseq, n, [sel], lambda b, p: synth.mkv_rows_of(seed, b, p))
+    out = plan.gather(0)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in [0, 33, 63]:
+        qc, qs = oracle.mkv_quantize(synth.mkv_rows_of(seed, np.full(k, b), sel[b]))
+        want, bad = oracle.mkv_gather(qc, qs, np.zeros(1, np.int64), np.array([k], np.int64),
+                                      np.arange(k, dtype=np.int32)[None, :])
+        assert bad == 0 and np.array_equal(got[b], want[0]), f"query {b}"

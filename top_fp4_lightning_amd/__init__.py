@@ -34,11 +34,15 @@ lib.idx_score_full.argtypes = [_P, _P, _P, _P, _i32, _i32, _i64, _P, _P, _P, _P,
 lib.idx_build_pool.argtypes = [_P, _i64, _P, _i32, _i64, _i32, _i32, _P, _i64, _P, _P, _sz, _P]
 lib.idx_score_pool_gather.argtypes = [_P, _P, _P, _P, _i32, _P, _i64, _P, _i32, _i32, _P, _P, _P, _P, _i64, _P, _P]
 lib.idx_topk.argtypes = [_P, _i64, _P, _i32, _i64, _i32, _P, _i64, _i32, _P, _i64, _P, _P, _sz, _P]
-for _f in ("idx_quantize_q", "idx_score_full", "idx_build_pool", "idx_score_pool_gather", "idx_topk"):
+lib.idx_quantize_kv.argtypes = [_P, _i64, _P, _P, _P]
+lib.idx_gather_kv.argtypes = [_P, _P, _P, _P, _i32, _P, _i64, _i32, _P, _P]
+for _f in ("idx_quantize_q", "idx_score_full", "idx_build_pool", "idx_score_pool_gather", "idx_topk",
+           "idx_quantize_kv", "idx_gather_kv"):
     getattr(lib, _f).restype = _i32
 
 EXPORTS = ("idx_abi_version", "idx_last_error", "idx_workspace_size", "idx_quantize_q", "idx_score_full",
-           "idx_build_pool", "idx_score_pool_gather", "idx_topk")
+           "idx_build_pool", "idx_score_pool_gather", "idx_topk", "idx_quantize_kv", "idx_gather_kv")
+MKV_DIM = 512
 
 
 class IdxError(RuntimeError):
@@ -150,3 +154,32 @@ def idx_topk(scores, max_n: int, k: int, out_idx, ws, n_valid=None, out_val=None
                         blocks.stride(0) if blocks is not None else 0, block, _ptr(out_idx), out_idx.stride(0),
                         _ptr(out_val), _ptr(ws), ws.numel(), _stream(stream)))
     return out_idx, out_val
+
+
+def idx_quantize_kv(x: torch.Tensor, codes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                    stream=None):
+    """Main-KV rows bf16 [..., 512] -> (codes [..., 256] u8, E4M3 scales [..., 32] u8)."""
+    _need(x, torch.bfloat16, "x")
+    lead = x.shape[:-1]
+    rows = x.numel() // MKV_DIM
+    if codes is None:
+        codes = torch.empty(*lead, MKV_DIM // 2, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(*lead, MKV_DIM // 16, dtype=torch.uint8, device=x.device)
+    _check(lib.idx_quantize_kv(_ptr(x), rows, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def idx_gather_kv(codes, scales, kv_base, n_vis, idx, out=None, k: int | None = None, stream=None):
+    """Selected main-KV entries dequantised: idx int32 [nq, >= k] -> bf16 [nq, k, 512]."""
+    _need(kv_base, torch.int64, "kv_base")
+    _need(n_vis, torch.int32, "n_vis")
+    _need(idx, torch.int32, "idx")
+    nq = idx.shape[0]
+    k = idx.shape[1] if k is None else k
+    if out is None:
+        out = torch.empty(nq, k, MKV_DIM, dtype=torch.bfloat16, device=idx.device)
+    _need(out, torch.bfloat16, "out")
+    _check(lib.idx_gather_kv(_ptr(codes), _ptr(scales), _ptr(kv_base), _ptr(n_vis), nq, _ptr(idx), idx.stride(0), k,
+                             _ptr(out), _stream(stream)))
+    return out

@@ -199,4 +199,30 @@ idx_status idx_topk(const float* scores, int64_t score_stride, const int32_t* n_
     return hip_status(launch_select(a, (hipStream_t)stream), "idx_topk");
 }
 
+
+idx_status idx_quantize_kv(const uint16_t* x_bf16, int64_t rows, uint8_t* codes, uint8_t* scales, void* stream) {
+    REQUIRE(rows >= 0 && rows <= (int64_t)1 << 31, IDX_EINVAL, "idx_quantize_kv: rows=%lld out of [0, 2^31]",
+            (long long)rows);
+    if (rows == 0) return ok();
+    REQUIRE(x_bf16 && codes && scales, IDX_EINVAL, "idx_quantize_kv: null pointer");
+    REQUIRE(aligned(x_bf16, 16) && aligned(codes, 4) && aligned(scales, 1), IDX_EALIGN,
+            "idx_quantize_kv: x must be 16-byte aligned, codes 4-byte aligned");
+    return hip_status(launch_quantize_kv(x_bf16, rows, codes, scales, (hipStream_t)stream), "idx_quantize_kv");
+}
+
+idx_status idx_gather_kv(const uint8_t* codes, const uint8_t* scales, const int64_t* kv_base, const int32_t* n_vis,
+                         int32_t nq, const int32_t* idx, int64_t idx_stride, int32_t k, uint16_t* out,
+                         void* stream) {
+    REQUIRE(nq >= 0 && k >= 0, IDX_EINVAL, "idx_gather_kv: nq=%d, k=%d must be >= 0", nq, k);
+    REQUIRE(nq <= kMaxQueries, IDX_EUNSUPPORTED, "idx_gather_kv: nq=%d above 65535", nq);
+    REQUIRE((int64_t)nq * k <= (int64_t)1 << 31, IDX_EUNSUPPORTED, "idx_gather_kv: nq * k above 2^31");
+    if (nq == 0 || k == 0) return ok();
+    REQUIRE(codes && scales && kv_base && n_vis && idx && out, IDX_EINVAL, "idx_gather_kv: null pointer");
+    REQUIRE(idx_stride >= k, IDX_EINVAL, "idx_gather_kv: idx_stride=%lld < k=%d", (long long)idx_stride, k);
+    REQUIRE(aligned(codes, 4) && aligned(kv_base, 8) && aligned(n_vis, 4) && aligned(idx, 4) && aligned(out, 16),
+            IDX_EALIGN, "idx_gather_kv: codes, n_vis and idx must be 4-byte, kv_base 8-byte, out 16-byte aligned");
+    return hip_status(launch_gather_kv(codes, scales, kv_base, n_vis, nq, idx, idx_stride, k, out, (hipStream_t)stream),
+                      "idx_gather_kv");
+}
+
 }  // extern "C"

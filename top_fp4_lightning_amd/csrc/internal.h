@@ -88,6 +88,12 @@ struct SelectArgs {
     void* ws;
 };
 size_t select_workspace_bytes(int32_t nq, int64_t max_n, int32_t k);
+
+// main-KV codec: rows of 512 values, E2M1 codes with an E4M3 scale per 16 values
+hipError_t launch_quantize_kv(const uint16_t* x, int64_t rows, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_gather_kv(const uint8_t* codes, const uint8_t* scales, const int64_t* kv_base, const int32_t* n_vis,
+                            int32_t nq, const int32_t* idx, int64_t idx_stride, int32_t k, uint16_t* out,
+                            hipStream_t stream);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 
 }  // namespace fp4idx

@@ -180,3 +180,41 @@ class PrefillPlan:
         idx_topk(self.cand_scores, self.kb * BLOCK, self.k, self.topk, self.ws_final, out_val=self.topk_val,
                  blocks=self.top_blocks, stream=stream)
         return self
+
+
+class MainKVGather:
+    """Main-KV gather for core attention: the FP4 main-KV cache of `nseq` sequences of `n`
+    entries each (one row per compressed position, 288 bytes) resident in HBM, and one
+    idx_gather_kv per selection (a layer's top-512 of every query) into preallocated bf16
+    buffers. Only the rows that the given selections touch are written at setup (quantised by
+    idx_quantize_kv from the supplied bf16 rows); the rest of the cache stays zero."""
+
+    def __init__(self, nseq: int, n: int, selections: list, rows_for, device="cuda", chunk: int = 1 << 16):
+        from . import MKV_DIM, idx_quantize_kv
+
+        self.nseq, self.n = nseq, n
+        total = nseq * n
+        self.codes = torch.zeros(total, MKV_DIM // 2, dtype=torch.uint8, device=device)
+        self.scales = torch.zeros(total, MKV_DIM // 16, dtype=torch.uint8, device=device)
+        self.kv_base = torch.arange(nseq, dtype=torch.int64, device=device) * n
+        self.n_vis = torch.full((nseq,), n, dtype=torch.int32, device=device)
+        self.sel = [torch.from_numpy(np.ascontiguousarray(s, dtype=np.int32)).to(device) for s in selections]
+        self.out = [torch.empty(s.shape[0], s.shape[1], MKV_DIM, dtype=torch.bfloat16, device=device)
+                    for s in selections]
+        # the distinct cache rows the selections read, written once
+        rows = np.unique(np.concatenate([(np.arange(s.shape[0])[:, None] * n + s).reshape(-1)[s.reshape(-1) >= 0]
+                                         for s in selections]).astype(np.int64))
+        self.rows_written = len(rows)
+        for r0 in range(0, len(rows), chunk):
+            part = rows[r0:r0 + chunk]
+            x = torch.from_numpy(rows_for(part // n, part % n).view(np.int16)).view(torch.bfloat16).to(device)
+            c, s = idx_quantize_kv(x)
+            dst = torch.from_numpy(part).to(device)
+            self.codes.index_copy_(0, dst, c)
+            self.scales.index_copy_(0, dst, s)
+
+    def gather(self, i: int, stream=None):
+        from . import idx_gather_kv
+
+        return idx_gather_kv(self.codes, self.scales, self.kv_base, self.n_vis, self.sel[i], out=self.out[i],
+                             stream=stream)
