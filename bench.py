@@ -189,6 +189,27 @@ def bench_decode(wl, args) -> int:
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1000.0 / args.steps
     scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms_eager = ms_step
+    if args.graph:
+        # the whole step captured once in a HIP graph (the plan allocates nothing and the library
+        # issues no memsets) and replayed: no per-launch host work inside the timed region
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            plan.run(stream=side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            plan.run(stream=torch.cuda.current_stream())
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1000.0 / args.steps
 
     n_vis = [int(x) for x in wl.n_vis]
     pool_pos = int(sum(min(n, 8 * min(2048, (n + 7) // 8)) for n in n_vis))
@@ -231,6 +252,8 @@ def bench_decode(wl, args) -> int:
         "top512_queries_per_s": queries / (ms_step / 1000.0),
         "full_scan_entries_per_s": int(sum(n_vis)) / (scan_ms / 1000.0),
         "scan_ms": scan_ms,
+        "step_launch": "hip graph replay" if args.graph else "eager launches",
+        "ms_per_step_eager": ms_eager,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
@@ -315,6 +338,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="fullscan_1m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode workloads: time replays of the step captured in a HIP graph")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 512 MiB device-to-device 5 times (calibrates the HBM byte counters)")
     args = ap.parse_args()
