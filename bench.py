@@ -262,6 +262,55 @@ def bench_decode(wl, args) -> int:
     return 0
 
 
+def bench_token(args) -> int:
+    """The indexer work of one decode token at 1M context, batch 8: the encoder's 3 Full layers
+    (8 x 2^19 keys each, own caches), then the decoder's Full layer (8 x 2^20), pool and 4 Reindex
+    layers. Per token 3 x 2.1e9 + 4.3e9 + 2.7e8 = 1.1e10 FP4 MACs ("DeepSeek-V4.1 model structure
+    (3)", the per-token totals with the candidate pool)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from top_fp4_lightning_amd import pipeline
+
+    t = time.perf_counter()
+    encs, dec = synth.token_1m()
+    plan = pipeline.TokenPlan([pipeline.DeviceWorkload.from_workload(w) for w in encs],
+                              pipeline.DeviceWorkload.from_workload(dec))
+    torch.cuda.synchronize()
+    log(f"token_1m: 3 encoder caches of {encs[0].total_keys} keys, decoder {dec.total_keys} keys; "
+        f"setup {time.perf_counter() - t:.1f} s")
+    for _ in range(args.warmup):
+        plan.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        plan.run()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1000.0 / args.steps
+    nb = dec.nq
+    enc_entries = sum(int(w.n_vis.sum()) for w in encs)
+    dec_entries = int(dec.n_vis.sum())
+    rei_entries = dec.layers * nb * 16384
+    entries = enc_entries + dec_entries + rei_entries
+    macs = 4096 * entries
+    queries = nb * (len(encs) + 1 + dec.layers)
+    res = {
+        "metric": "indexer entries scored/s + top-512 queries/s for one decode token at 1M ctx (all 8 indexer layers)",
+        "value": entries / (ms_step / 1000.0), "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp4",
+        "data": "synthetic (seeded N(0,1) bf16 q/k, N(0,1/32) w, 1% planted keys; no trained weights)",
+        "config": {"workload": "token_1m: batch 8; encoder 3 Full layers x 2^19 keys (m=2, own caches) + decoder "
+                               "Full 2^20 + pool(2048 blocks of 8) + 4 Reindex layers", "batch": nb},
+        "fp4_macs_per_token": macs / nb,
+        "top512_queries_per_s": queries / (ms_step / 1000.0),
+        "macs_per_s": macs / (ms_step / 1000.0),
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_kv_gather(args) -> int:
     """Main-KV gather for core attention at the Reindex decode shape: 64 sequences x 2^20
     compressed entries of FP4 main KV resident in HBM (288 bytes each); one step gathers the
@@ -367,6 +416,8 @@ def main() -> int:
         return 0
     if args.workload == "kv_gather_1m":
         return bench_kv_gather(args)
+    if args.workload == "token_1m":
+        return bench_token(args)
     wl = synth.config(args.workload)
     if args.workload == "prefill_128k":
         return bench_prefill(wl, args)

@@ -307,7 +307,16 @@ def config(name: str) -> Workload:
         return prefill_workload(name, 5, 131072, 4096)
     if name == "spec_decode_1m":  # 8 x 2^20, the token + 5 draft positions per sequence, 4 Reindex layers
         return spec_decode_workload(name, 6, [1 << 20] * 8, positions=6, layers=4)
+    if name.startswith("encoder_512k_l") and name[-1] in "012":  # encoder Full layer l: its own 8 x 2^19 keys
+        return decode_workload(name, 60 + int(name[-1]), [1 << 19] * 8)
     raise KeyError(name)
+
+
+def token_1m() -> tuple:
+    """The indexer work of one decode token at 1M context for a batch of 8: the encoder's 3 Full
+    layers (m = 2, each over its own 2^19-entry key cache) and the decoder's layer-20 Full scan
+    with the candidate pool and 4 Reindex layers (m = 1, 2^20 entries)."""
+    return [config(f"encoder_512k_l{i}") for i in range(3)], config("fullscan_1m")
 
 
 CONFIGS = ("decode_32k", "decode_batch64", "reindex_1m", "fullscan_1m", "fullscan_512k", "prefill_128k",

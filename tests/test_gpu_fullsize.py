@@ -135,6 +135,20 @@ def test_spec_decode_1m(pl):
     check_decode_queries(wl, out, sample=[0, 5, 46])
 
 
+def test_token_1m_encoder_layers(pl):
+    # the per-token schedule: 3 encoder Full layers over their own 8 x 2^19 caches, then the
+    # decoder step; sampled encoder queries against the oracle (the decoder part is
+    # test_fullscan_1m's)
+    encs, dec = synth.token_1m()
+    plan = pl.TokenPlan([pl.DeviceWorkload.from_workload(w) for w in encs], pl.DeviceWorkload.from_workload(dec))
+    plan.run()
+    torch.cuda.synchronize()
+    for wl, p, t in [(encs[0], plan.encoders[0], 2), (encs[2], plan.encoders[2], 6)]:
+        out = {"topk": p.topk[0], "topk_val": p.topk_val[0], "pool_blocks": p.pool_blocks,
+               "pool_count": p.pool_count, "block_max": p.block_max, "reindex_topk": []}
+        check_decode_queries(wl, out, sample=[t])
+
+
 def test_prefill_128k(pl):
     # 4096 queries on 131072 keys, query i sees positions <= 126976 + i
     wl = synth.config("prefill_128k")

@@ -59,3 +59,13 @@ def test_spec_decode_shape():
     assert np.array_equal(w.n_vis[:6], (1 << 20) - 5 + np.arange(6))
     assert (w.k_base[6:12] == 1 << 20).all() and (w.k_base[:6] == 0).all()
     assert np.array_equal(w.plant_query, np.arange(8) * 6)
+
+
+def test_token_schedule_shape_and_page_total():
+    # 3 encoder Full layers (own caches, m = 2) + decoder Full + 4 Reindex layers over the pool:
+    # 3 x 2^19 x 4096 + 2^20 x 4096 + 4 x 16384 x 4096 MACs per token = 1.1e10 (the page's total)
+    encs, dec = synth.token_1m()
+    assert len(encs) == 3 and all(w.nq == 8 and (w.n_vis == 1 << 19).all() for w in encs)
+    assert len({w.seed for w in encs}) == 3 and dec.layers == 4 and (dec.n_vis == 1 << 20).all()
+    macs = (sum(int(w.n_vis[0]) for w in encs) + int(dec.n_vis[0]) + dec.layers * 16384) * 4096
+    assert float(f"{macs:.1e}") == 1.1e10

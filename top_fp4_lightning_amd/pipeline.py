@@ -134,6 +134,25 @@ class DecodePlan:
         return self
 
 
+class TokenPlan:
+    """The indexer work of one decode token across the model ("DeepSeek-V4.1 model structure
+    (3)", the per-token table of section "Reindex layers score a million entries per token", and
+    section "it is only in the decoder"): each encoder Full layer scans its own key cache and keeps
+    its own top-512 (no pool in the encoder; the plan reaches the exact top-512 through block maxima
+    and a gather, as for the decoder's Full layer), then the decoder's Full layer, pool and Reindex
+    layers."""
+
+    def __init__(self, encoders: list, decoder: DeviceWorkload, k: int = 512):
+        self.encoders = [DecodePlan(d, k=k) for d in encoders]
+        self.decoder = DecodePlan(decoder, k=k)
+
+    def run(self, stream=None):
+        for p in self.encoders:
+            p.run(stream)
+        self.decoder.run(stream)
+        return self
+
+
 def decode_step(dev: DeviceWorkload, plan: DecodePlan | None = None, **kw) -> dict:
     plan = plan or DecodePlan(dev, **kw)
     plan.run()
