@@ -68,6 +68,7 @@ def lib():
         L.orc_mkv_value.restype = d
         L.orc_mkv_gather.argtypes = [P, P, P, P, P, i32, i32, i64, P]
         L.orc_mkv_gather.restype = i64
+        L.orc_mask_pool.argtypes = [P, i64, P, i32, i32, P]
         L.orc_reindex_mask.argtypes = [P, i64, P, i32, i32, i32, P]
         L.orc_reindex_mask.restype = i32
         L.orc_reindex_gather.argtypes = [P, P, P, P, P, i64, P, i32, i32, i32, P]
@@ -284,3 +285,12 @@ def mkv_gather(codes, scales, base, n, idx):
     out = np.empty((nq, k, MKV_DIM), dtype=np.uint16)
     bad = lib().orc_mkv_gather(_p(codes), _p(scales), _p(base), _p(n), _p(idx), nq, k, k, _p(out))
     return out, int(bad)
+
+
+def mask_pool(I_full: np.ndarray, pool_blocks: np.ndarray, block: int = 8) -> np.ndarray:
+    """the pool applied as the official code does: -inf outside the pooled blocks (fp64)"""
+    I = np.ascontiguousarray(I_full, dtype=np.float64)
+    pb = np.ascontiguousarray(pool_blocks, dtype=np.int32)
+    out = np.empty(len(I))
+    lib().orc_mask_pool(_p(I), len(I), _p(pb), len(pb), block, _p(out))
+    return out

@@ -346,15 +346,22 @@ int32_t orc_pool(const double* bm, int64_t n, int32_t block, int32_t topk_blocks
     return cnt;
 }
 
+/* the pool as the official code applies it: every visible position outside the pooled blocks
+ * set to -inf, pooled positions keep their score */
+void orc_mask_pool(const double* I_full, int64_t n, const int32_t* pool_blocks, int32_t count, int32_t block,
+                   double* m) {
+    for (int64_t s = 0; s < n; ++s) m[s] = -INFINITY;
+    for (int32_t i = 0; i < count; ++i)
+        for (int64_t s = (int64_t)pool_blocks[i] * block; s < ((int64_t)pool_blocks[i] + 1) * block && s < n; ++s)
+            if (s >= 0) m[s] = I_full[s];
+}
+
 /* Reindex, mask form: scores of every visible position, non-pool positions set to -inf, then
  * top-k of what is left */
 int32_t orc_reindex_mask(const double* I_full, int64_t n, const int32_t* pool_blocks, int32_t count,
                          int32_t block, int32_t k, int32_t* out) {
     double* m = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
-    for (int64_t s = 0; s < n; ++s) m[s] = -INFINITY;
-    for (int32_t i = 0; i < count; ++i)
-        for (int64_t s = (int64_t)pool_blocks[i] * block; s < ((int64_t)pool_blocks[i] + 1) * block && s < n; ++s)
-            m[s] = I_full[s];
+    orc_mask_pool(I_full, n, pool_blocks, count, block, m);
     int32_t r = orc_topk(m, n, k, out);
     free(m);
     return r;

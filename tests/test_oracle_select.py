@@ -150,3 +150,18 @@ def test_decode_batch_matches_pieces():
         for li in range(2):
             Il, _ = oracle.score_rows(rq[li][0][t], rq[li][1][t], w.w(li + 1)[t], kc[b0:b0 + nn], ks[b0:b0 + nn])
             assert np.array_equal(rtop[li, t], oracle.reindex_mask(Il, pool))
+
+
+@pytest.mark.parametrize("n,count", [(1, 1), (100, 5), (1000, 125), (4097, 300)])
+def test_mask_pool_keeps_exactly_the_pooled_positions(n, count):
+    rng = np.random.default_rng(n + count)
+    I = rng.standard_normal(n)
+    nb = (n + 7) // 8
+    pool = rng.permutation(nb)[:min(count, nb)].astype(np.int32)
+    m = oracle.mask_pool(I, pool)
+    blocks = np.arange(n) // 8
+    inside = np.isin(blocks, pool)
+    assert np.array_equal(m[inside], I[inside]) and np.isneginf(m[~inside]).all()
+    assert inside.sum() == sum(min(8, n - 8 * int(b)) for b in pool)
+    # the official form: a boolean table per query; masking and top-k equals the mask-form Reindex
+    assert np.array_equal(oracle.topk(m, 7), oracle.reindex_mask(I, pool, 8, 7))
