@@ -262,6 +262,71 @@ def bench_decode(wl, args) -> int:
     return 0
 
 
+def bench_mask_form(args) -> int:
+    """The decode step at fullscan_1m in the pool's training form, all 5 layers batched: one
+    many-query scan writes every layer's full score row (8 x 5 rows of 2^20), then the pool, the
+    mask and a top-512 per row ("DeepSeek-V4.1 model structure (3)", sections "three details of
+    the pool in the code" and "the pool also acts in training"). The gather form (the inference
+    step of bench_decode) is timed beside it on the same resident inputs; both give the same
+    selections. The roofline is the scan's FP4 matrix rate."""
+    import numpy as np
+    import torch
+
+    import synth
+    from top_fp4_lightning_amd import pipeline
+
+    wl = synth.config("fullscan_1m")
+    t = time.perf_counter()
+    dev = pipeline.DeviceWorkload.from_workload(wl)
+    mask = pipeline.MaskFormPlan(dev)
+    gather = pipeline.DecodePlan(dev)
+    torch.cuda.synchronize()
+    log(f"mask_form_1m: {wl.nq} queries x {mask.L} layers, {wl.total_keys} keys; setup {time.perf_counter() - t:.1f} s")
+
+    def timed(run, steps, ev=None):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            run(None if ev is None else ev[i])
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1000.0 / steps
+
+    def mask_step(e=None):
+        mask.run(events=e)
+
+    timed(mask_step, args.warmup)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ms_mask = timed(mask_step, args.steps, evs)
+    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    timed(lambda e: gather.run(), args.warmup)
+    ms_gather = timed(lambda e: gather.run(), args.steps)
+    n_vis = [int(x) for x in wl.n_vis]
+    entries = mask.L * int(sum(n_vis))
+    flop = 2.0 * 4096.0 * entries
+    achieved = flop / (scan_ms / 1000.0) / 1e12
+    sb = int(sum(n_vis)) * 68 + mask.rows * (32 * 68 + 32 * 4) + entries * 4 + mask.L * sum((n + 7) // 8 for n in n_vis) * 4
+    res = {
+        "metric": "indexer entries scored/s + top-512 queries/s at 1M ctx, training form (mask after full scan)",
+        "value": entries / (ms_mask / 1000.0), "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_mask, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp4",
+        "data": "synthetic (seeded N(0,1) bf16 q/k, N(0,1/32) w, 1% planted keys; no trained weights)",
+        "config": {"workload": "mask_form_1m: 8 x 1048576 keys, Full + 4 Reindex layers each scoring every "
+                               "position in one many-query scan, pool mask, top-512 per layer", "batch": wl.nseq,
+                   "layers": mask.L, "k": 512, "pool_blocks": 2048, "block": 8},
+        "top512_queries_per_s": mask.rows / (ms_mask / 1000.0),
+        "scan_ms": scan_ms,
+        "gather_form_ms_per_step": ms_gather,
+        "mask_over_gather": ms_mask / ms_gather,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_FP4_PEAK_TFLOPS, "traffic": None, "kernel": "score_multi_kernel",
+                     "algorithmic_flop_per_launch": flop, "algorithmic_bytes_per_launch": sb,
+                     "hbm_achieved_gbs": sb / (scan_ms / 1000.0) / 1e9},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_token(args) -> int:
     """The indexer work of one decode token at 1M context, batch 8: the encoder's 3 Full layers
     (8 x 2^19 keys each, own caches), then the decoder's Full layer (8 x 2^20), pool and 4 Reindex
@@ -418,6 +483,8 @@ def main() -> int:
         return bench_kv_gather(args)
     if args.workload == "token_1m":
         return bench_token(args)
+    if args.workload == "mask_form_1m":
+        return bench_mask_form(args)
     wl = synth.config(args.workload)
     if args.workload == "prefill_128k":
         return bench_prefill(wl, args)

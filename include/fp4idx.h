@@ -205,6 +205,32 @@ idx_status idx_topk(const float* scores, int64_t score_stride, const int32_t* n_
                     int64_t out_stride, float* out_val, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * idx_mask_pool: the candidate pool in its training form ([P1] "three details of the pool in the
+ * code": the official code turns the pool into a boolean table and a Reindex layer sets every
+ * score outside it to -inf before its top-512; "the pool also acts in training": post-training
+ * applies the same restriction). In place: with p = t / group, scores[t][s] = -inf for every
+ * visible position s < n_t whose block s / block is not among pool_blocks[p][0 .. pool_count[p] - 1];
+ * pooled positions and positions >= n_t are left as they are. With idx_score_full (scores)
+ * before it and idx_topk after it, this is the mask-form Reindex layer; its top-512 equals the
+ * gather form (idx_score_pool_gather + idx_topk with the block map). `group` lets the rows of
+ * several layers of one query (consecutive rows) share that query's pool.
+ *
+ *   scores      : device fp32 [nq][score_stride], read and written; score_stride >= max_n.
+ *   n_vis, max_n: as for idx_score_full (max_n up to 2^30).
+ *   pool_blocks : device int32 [nq / group][pool_stride] block ids in any order (ids outside the
+ *                 row are ignored); pool_count : device int32 [nq / group], clamped to
+ *                 [0, pool_stride].
+ *   group       : >= 1 and divides nq.
+ *   block       : must be 8.
+ * Errors: IDX_EINVAL (null pointer, score_stride < max_n, negative pool_stride, group not
+ * dividing nq), IDX_EALIGN (pointers not 4-byte aligned), IDX_EUNSUPPORTED (nq > 65535,
+ * max_n > 2^30, block != 8); nothing is launched on error. nq == 0 or max_n == 0 is a no-op.
+ */
+idx_status idx_mask_pool(float* scores, int64_t score_stride, const int32_t* n_vis, int32_t nq, int64_t max_n,
+                         const int32_t* pool_blocks, int64_t pool_stride, const int32_t* pool_count, int32_t group,
+                         int32_t block, void* stream);
+
+/*
  * Main-KV FP4 storage ([P1] "the scale format decides precision" and "removing the global scale
  * still leaves enough range"): a main-KV entry is 512 values stored as E2M1 codes (element 2i in
  * the low nibble of byte i) with one E4M3 scale per group of 16 values and no global scale,

@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["idx_quantize_q", "idx_score_full", "idx_build_pool", "idx_score_pool_gather", "idx_topk",
-              "idx_last_error", "idx_abi_version", "idx_workspace_size", "idx_quantize_kv", "idx_gather_kv"]:
+              "idx_last_error", "idx_abi_version", "idx_workspace_size", "idx_quantize_kv", "idx_gather_kv", "idx_mask_pool"]:
         assert n in names
 
 
@@ -168,6 +168,28 @@ def test_main_kv_validation(fx):
     assert g(*bad) == fx.IDX_EUNSUPPORTED
     bad = list(good); bad[7] = -1
     assert g(*bad) == fx.IDX_EINVAL
+
+
+def test_mask_pool_validation(fx):
+    m = lambda *a: call(fx, "idx_mask_pool", *a)[0]
+    good = [FAKE, 4096, FAKE, 10, 4096, FAKE, 2048, FAKE, 5, 8, None]
+    assert m(*[None, 0, None, 0, 0, None, 0, None, 1, 8, None]) == fx.IDX_OK  # empty is a no-op
+    bad = list(good); bad[0] = None
+    assert m(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[1] = 100  # score_stride < max_n
+    assert m(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[8] = 3  # group does not divide nq
+    assert m(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[8] = 0
+    assert m(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[6] = -1
+    assert m(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[9] = 16
+    assert m(*bad) == fx.IDX_EUNSUPPORTED
+    bad = list(good); bad[3] = 70000; bad[8] = 1
+    assert m(*bad) == fx.IDX_EUNSUPPORTED
+    bad = list(good); bad[0] = FAKE + 2
+    assert m(*bad) == fx.IDX_EALIGN
 
 
 def test_python_binding_refuses_cpu_tensors(fx):

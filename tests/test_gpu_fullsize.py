@@ -105,6 +105,23 @@ def test_fullscan_1m(pl):
     check_decode_queries(wl, out, sample=[0, 7])
 
 
+def test_mask_form_fullscan_1m(pl):
+    # the training form at the benchmark's workload: every layer scores all 2^20 positions, the
+    # pool masks them; pools and every layer's top-512 equal the gather form's (whose selections
+    # test_fullscan_1m pins to the oracle)
+    wl = synth.config("fullscan_1m")
+    dev = pl.DeviceWorkload.from_workload(wl)
+    gather = pl.DecodePlan(dev).run()
+    mask = pl.MaskFormPlan(dev).run()
+    torch.cuda.synchronize()
+    assert torch.equal(mask.pool_count, gather.pool_count)
+    assert torch.equal(mask.pool_blocks, gather.pool_blocks)
+    for layer in range(mask.L):
+        mi, mv = mask.layer_topk(layer)
+        assert torch.equal(mi, gather.topk[layer]), f"layer {layer}"
+        assert torch.equal(mv, gather.topk_val[layer]), f"layer {layer}"
+
+
 def test_fullscan_512k(pl):
     # 8 x 2^19 keys (encoder shape, m = 2)
     wl = synth.config("fullscan_512k")

@@ -36,12 +36,14 @@ lib.idx_score_pool_gather.argtypes = [_P, _P, _P, _P, _i32, _P, _i64, _P, _i32, 
 lib.idx_topk.argtypes = [_P, _i64, _P, _i32, _i64, _i32, _P, _i64, _i32, _P, _i64, _P, _P, _sz, _P]
 lib.idx_quantize_kv.argtypes = [_P, _i64, _P, _P, _P]
 lib.idx_gather_kv.argtypes = [_P, _P, _P, _P, _i32, _P, _i64, _i32, _P, _P]
+lib.idx_mask_pool.argtypes = [_P, _i64, _P, _i32, _i64, _P, _i64, _P, _i32, _i32, _P]
 for _f in ("idx_quantize_q", "idx_score_full", "idx_build_pool", "idx_score_pool_gather", "idx_topk",
-           "idx_quantize_kv", "idx_gather_kv"):
+           "idx_quantize_kv", "idx_gather_kv", "idx_mask_pool"):
     getattr(lib, _f).restype = _i32
 
 EXPORTS = ("idx_abi_version", "idx_last_error", "idx_workspace_size", "idx_quantize_q", "idx_score_full",
-           "idx_build_pool", "idx_score_pool_gather", "idx_topk", "idx_quantize_kv", "idx_gather_kv")
+           "idx_build_pool", "idx_score_pool_gather", "idx_topk", "idx_quantize_kv", "idx_gather_kv",
+           "idx_mask_pool")
 MKV_DIM = 512
 
 
@@ -63,6 +65,17 @@ def _ptr(t: torch.Tensor | None) -> int | None:
         raise ValueError("fp4idx tensors must live on the GPU")
     if not t.is_contiguous():
         raise ValueError("fp4idx tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _rows_ptr(t: torch.Tensor | None) -> int | None:
+    """A 2-D argument the library reads through its own row stride: each row contiguous."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("fp4idx tensors must live on the GPU")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("fp4idx row arguments must be 2-D with contiguous rows")
     return t.data_ptr()
 
 
@@ -118,8 +131,9 @@ def idx_score_full(k_codes, k_scales, k_base, n_vis, q_codes, q_scales, w, max_n
     ss = scores.stride(0) if scores is not None else (head_dots.shape[-1] if head_dots is not None else 0)
     bs = block_max.stride(0) if block_max is not None else 0
     _check(lib.idx_score_full(_ptr(k_codes), _ptr(k_scales), _ptr(k_base), _ptr(n_vis), nq, group, max_n,
-                              _ptr(q_codes), _ptr(q_scales), _ptr(w), _ptr(scores), ss, _ptr(block_max), bs,
-                              _ptr(head_dots), _stream(stream)))
+                              _ptr(q_codes), _ptr(q_scales), _ptr(w),
+                              _ptr(scores) if head_dots is not None else _rows_ptr(scores), ss,
+                              _rows_ptr(block_max), bs, _ptr(head_dots), _stream(stream)))
     return scores, block_max, head_dots
 
 
@@ -128,7 +142,7 @@ def idx_build_pool(block_max, n_vis, max_n: int, pool_blocks, pool_count, ws, to
     nq = n_vis.shape[0]
     _need(block_max, torch.float32, "block_max")
     _need(pool_blocks, torch.int32, "pool_blocks")
-    _check(lib.idx_build_pool(_ptr(block_max), block_max.stride(0), _ptr(n_vis), nq, max_n, topk_blocks, block,
+    _check(lib.idx_build_pool(_rows_ptr(block_max), block_max.stride(0), _ptr(n_vis), nq, max_n, topk_blocks, block,
                               _ptr(pool_blocks), pool_blocks.stride(0), _ptr(pool_count), _ptr(ws), ws.numel(),
                               _stream(stream)))
     return pool_blocks, pool_count
@@ -138,9 +152,11 @@ def idx_score_pool_gather(k_codes, k_scales, k_base, n_vis, blocks, block_count,
                           q_scales, w, scores, head_dots=None, block: int = BLOCK, stream=None):
     nq = n_vis.shape[0]
     _need(scores, torch.float32, "scores")
-    _check(lib.idx_score_pool_gather(_ptr(k_codes), _ptr(k_scales), _ptr(k_base), _ptr(n_vis), nq, _ptr(blocks),
+    _check(lib.idx_score_pool_gather(_ptr(k_codes), _ptr(k_scales), _ptr(k_base), _ptr(n_vis), nq, _rows_ptr(blocks),
                                      blocks.stride(0), _ptr(block_count), max_blocks, block, _ptr(q_codes),
-                                     _ptr(q_scales), _ptr(w), _ptr(scores), scores.stride(0), _ptr(head_dots),
+                                     _ptr(q_scales), _ptr(w),
+                                     _ptr(scores) if head_dots is not None else _rows_ptr(scores), scores.stride(0),
+                                     _ptr(head_dots),
                                      _stream(stream)))
     return scores
 
@@ -150,7 +166,7 @@ def idx_topk(scores, max_n: int, k: int, out_idx, ws, n_valid=None, out_val=None
     nq = scores.shape[0]
     _need(scores, torch.float32, "scores")
     _need(out_idx, torch.int32, "out_idx")
-    _check(lib.idx_topk(_ptr(scores), scores.stride(0), _ptr(n_valid), nq, max_n, k, _ptr(blocks),
+    _check(lib.idx_topk(_rows_ptr(scores), scores.stride(0), _ptr(n_valid), nq, max_n, k, _rows_ptr(blocks),
                         blocks.stride(0) if blocks is not None else 0, block, _ptr(out_idx), out_idx.stride(0),
                         _ptr(out_val), _ptr(ws), ws.numel(), _stream(stream)))
     return out_idx, out_val
@@ -183,3 +199,15 @@ def idx_gather_kv(codes, scales, kv_base, n_vis, idx, out=None, k: int | None = 
     _check(lib.idx_gather_kv(_ptr(codes), _ptr(scales), _ptr(kv_base), _ptr(n_vis), nq, _ptr(idx), idx.stride(0), k,
                              _ptr(out), _stream(stream)))
     return out
+
+
+def idx_mask_pool(scores, n_vis, max_n: int, pool_blocks, pool_count, group: int = 1, block: int = BLOCK,
+                  stream=None):
+    """In place: -inf at every visible position outside the pooled blocks (the pool's training
+    form); score row t uses pool row t // group."""
+    _need(scores, torch.float32, "scores")
+    _need(pool_blocks, torch.int32, "pool_blocks")
+    nq = n_vis.shape[0]
+    _check(lib.idx_mask_pool(_rows_ptr(scores), scores.stride(0), _ptr(n_vis), nq, max_n, _rows_ptr(pool_blocks),
+                             pool_blocks.stride(0), _ptr(pool_count), group, block, _stream(stream)))
+    return scores

@@ -7,7 +7,7 @@ import tempfile
 from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["api.hip", "quantize.hip", "score.hip", "score_multi.hip", "select.hip", "mainkv.hip"]
+SOURCES = ["api.hip", "quantize.hip", "score.hip", "score_multi.hip", "select.hip", "mainkv.hip", "mask.hip"]
 OUT = os.path.join(HERE, "libfp4idx.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -225,4 +225,24 @@ idx_status idx_gather_kv(const uint8_t* codes, const uint8_t* scales, const int6
                       "idx_gather_kv");
 }
 
+idx_status idx_mask_pool(float* scores, int64_t score_stride, const int32_t* n_vis, int32_t nq, int64_t max_n,
+                         const int32_t* pool_blocks, int64_t pool_stride, const int32_t* pool_count, int32_t group,
+                         int32_t block, void* stream) {
+    REQUIRE(nq >= 0 && nq <= kMaxQueries, IDX_EUNSUPPORTED, "idx_mask_pool: nq=%d out of [0, 65535]", nq);
+    REQUIRE(max_n >= 0 && max_n <= kMaxN, IDX_EUNSUPPORTED, "idx_mask_pool: max_n=%lld out of [0, 2^30]",
+            (long long)max_n);
+    REQUIRE(block == kBlock, IDX_EUNSUPPORTED, "idx_mask_pool: block=%d (only %d)", block, kBlock);
+    REQUIRE(group >= 1 && (nq == 0 || nq % group == 0), IDX_EINVAL, "idx_mask_pool: group=%d must divide nq=%d",
+            group, nq);
+    if (nq == 0 || max_n == 0) return ok();
+    REQUIRE(scores && n_vis && pool_blocks && pool_count, IDX_EINVAL, "idx_mask_pool: null pointer");
+    REQUIRE(score_stride >= max_n, IDX_EINVAL, "idx_mask_pool: score_stride=%lld < max_n", (long long)score_stride);
+    REQUIRE(pool_stride >= 0, IDX_EINVAL, "idx_mask_pool: negative pool_stride");
+    REQUIRE(aligned(scores, 4) && aligned(n_vis, 4) && aligned(pool_blocks, 4) && aligned(pool_count, 4), IDX_EALIGN,
+            "idx_mask_pool: pointers must be 4-byte aligned");
+    return hip_status(launch_mask_pool(scores, score_stride, n_vis, nq, max_n, pool_blocks, pool_stride, pool_count,
+                                       group, (hipStream_t)stream),
+                      "idx_mask_pool");
+}
+
 }  // extern "C"

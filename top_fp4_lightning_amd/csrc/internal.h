@@ -89,6 +89,11 @@ struct SelectArgs {
 };
 size_t select_workspace_bytes(int32_t nq, int64_t max_n, int32_t k);
 
+// training form of the pool: -inf outside the pooled blocks, in place
+hipError_t launch_mask_pool(float* scores, int64_t score_stride, const int32_t* n_vis, int32_t nq, int64_t max_n,
+                            const int32_t* pool_blocks, int64_t pool_stride, const int32_t* pool_count,
+                            int32_t group, hipStream_t stream);
+
 // main-KV codec: rows of 512 values, E2M1 codes with an E4M3 scale per 16 values
 hipError_t launch_quantize_kv(const uint16_t* x, int64_t rows, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t launch_gather_kv(const uint8_t* codes, const uint8_t* scales, const int64_t* kv_base, const int32_t* n_vis,

@@ -15,6 +15,12 @@ Several queries per sequence (speculative verification of the draft positions, "
 inference-side full breakdown", section 8.2): the same decode step with group = positions per
 sequence, so the Full scan reads each key once for all of them (the many-query scan).
 
+Training form ("DeepSeek-V4.1 model structure (3)", sections "three details of the pool in the
+code" and "the pool also acts in training"): every layer scores every visible position, and a
+Reindex layer sets the scores outside the pool to -inf before its top-512. MaskFormPlan runs it for
+all layers at once (the queries of every layer present together): one scan of the key cache
+serves every layer's query, then the pool, the mask and one top-512 per row.
+
 Prefill (a chunk of queries sharing one key range, causal): idx_score_full writes block maxima
 for every query; idx_topk keeps the 512 best blocks per query (a top-512 key's block is among
 them); idx_score_pool_gather re-scores those 4096 keys; idx_topk takes the final 512.
@@ -29,8 +35,8 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from . import (BLOCK, IDX_OP_BUILD_POOL, IDX_OP_TOPK, idx_build_pool, idx_quantize_q, idx_score_full,
-               idx_score_pool_gather, idx_topk, workspace)
+from . import (BLOCK, IDX_OP_BUILD_POOL, IDX_OP_TOPK, idx_build_pool, idx_mask_pool, idx_quantize_q,
+               idx_score_full, idx_score_pool_gather, idx_topk, workspace)
 
 
 @dataclass
@@ -159,6 +165,59 @@ def decode_step(dev: DeviceWorkload, plan: DecodePlan | None = None, **kw) -> di
     return {"topk": plan.topk[0], "topk_val": plan.topk_val[0], "pool_blocks": plan.pool_blocks,
             "pool_count": plan.pool_count, "block_max": plan.block_max,
             "reindex_topk": plan.topk[1:], "plan": plan}
+
+
+class MaskFormPlan:
+    """The decode step in its training form, all layers batched. Rows are stacked query-major
+    (row = query * L + layer, L = Full layer + Reindex layers), so the rows of one key range stay
+    consecutive and one many-query scan computes every layer's full score row (and the block
+    maxima the Full layer's pool is built from). The mask then applies each query's pool to all
+    of its rows. On the Full layer's row it changes no top-512 entry: a key outside the pool is
+    outranked by a key of each of the 2047 unpinned pooled blocks (their maxima beat or tie-win
+    its block's), so it never makes the top-512. The results equal DecodePlan's gather form."""
+
+    def __init__(self, dev: DeviceWorkload, k: int = 512, topk_blocks: int = 2048):
+        nq, max_n = dev.nq, dev.max_n
+        d = dev.k_codes.device
+        self.dev, self.k, self.topk_blocks = dev, k, topk_blocks
+        self.L = L = len(dev.q)
+        self.rows = rows = nq * L
+        nb = (max_n + BLOCK - 1) // BLOCK
+        self.q = torch.stack(dev.q, 1).reshape(rows, 32, 128).contiguous()
+        self.w = torch.stack(dev.w, 1).reshape(rows, 32).contiguous()
+        self.k_base = dev.k_base.repeat_interleave(L)
+        self.n_vis = dev.n_vis.repeat_interleave(L)
+        self.q_codes = torch.empty(rows, 32, 64, dtype=torch.uint8, device=d)
+        self.q_scales = torch.empty(rows, 32, 4, dtype=torch.uint8, device=d)
+        self.scores = torch.empty(rows, max(max_n, 1), dtype=torch.float32, device=d)
+        self.block_max = torch.empty(rows, max(nb, 1), dtype=torch.float32, device=d)
+        self.pool_blocks = torch.empty(nq, topk_blocks, dtype=torch.int32, device=d)
+        self.pool_count = torch.empty(nq, dtype=torch.int32, device=d)
+        self.topk = torch.empty(rows, k, dtype=torch.int32, device=d)
+        self.topk_val = torch.empty(rows, k, dtype=torch.float32, device=d)
+        self.ws_pool = workspace(IDX_OP_BUILD_POOL, nq, max_n, topk_blocks, device=d)
+        self.ws_topk = workspace(IDX_OP_TOPK, rows, max(max_n, 1), k, device=d)
+
+    def layer_topk(self, layer: int):
+        """(indices, values) [nq, k] of one layer."""
+        return self.topk.view(-1, self.L, self.k)[:, layer], self.topk_val.view(-1, self.L, self.k)[:, layer]
+
+    def run(self, stream=None, events=None):
+        dv, L = self.dev, self.L
+        idx_quantize_q(self.q, dv.signs, self.q_codes, self.q_scales, stream=stream)
+        if events is not None:
+            events[0].record()
+        idx_score_full(dv.k_codes, dv.k_scales, self.k_base, self.n_vis, self.q_codes, self.q_scales, self.w,
+                       dv.max_n, group=dv.group * L, scores=self.scores, block_max=self.block_max, stream=stream)
+        if events is not None:
+            events[1].record()
+        full_bm = self.block_max.view(dv.nq, L, -1)[:, 0]  # the Full layer's rows
+        idx_build_pool(full_bm, dv.n_vis, dv.max_n, self.pool_blocks, self.pool_count, self.ws_pool,
+                       topk_blocks=self.topk_blocks, stream=stream)
+        idx_mask_pool(self.scores, self.n_vis, dv.max_n, self.pool_blocks, self.pool_count, group=L, stream=stream)
+        idx_topk(self.scores, dv.max_n, self.k, self.topk, self.ws_topk, n_valid=self.n_vis, out_val=self.topk_val,
+                 stream=stream)
+        return self
 
 
 class PrefillPlan:
