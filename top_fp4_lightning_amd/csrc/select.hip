@@ -337,139 +337,364 @@ __device__ __forceinline__ void write_pad(const SelectArgs& a, int64_t t, uint32
     if (a.out_count && threadIdx.x == 0) a.out_count[t] = (int32_t)cnt;
 }
 
-// ---------------------------------------------------------------- rows of <= 16384 values
-// One block per row, 16 composites per thread in registers; the block size follows the row
-// capacity (256 threads up to 4096 values, 512 up to 8192, 1024 up to 16384) so that many short
-// rows keep many blocks resident.
-constexpr int kRowPer = 16;
-constexpr int kListMax = 4096;  // LDS candidates for the wave-level passes
+// ---------------------------------------------------------------- rows of <= 16 * NT values
+// One block per row. Thread tid holds the values of slots 8 * (tid + r * NT) + e (run r < 2,
+// e < 8) in registers (-inf past the row, +inf for the pinned block) and the position of each
+// run's first slot. Work per value is a handful of instructions; everything else runs on a short
+// candidate list:
+//  1. A lower bound T0 of the k-th largest key: each wavefront takes the R-th largest of its
+//     lanes' maxima, R = ceil(k / wavefronts), so at least R lanes of every wavefront (k values
+//     in all) hold a value at or above the smallest of these.
+//  2. The values at or above T0 (a few percent of a row) go to an LDS list in slot order, as
+//     (value bits, ~position).
+//  3. Radix passes over the list find T: the first digit starts below the bits that T0 and the
+//     row maximum share; passes stop when the threshold digit holds exactly the elements still
+//     needed, or at most 64 of them, which are then ranked against each other in parallel.
+//  4. The list entries >= T are written in list order.
+// When R > 64 or the candidates overflow the list, the radix passes run over the registers
+// (wave-private histograms) and the winners are compacted from the registers.
+constexpr int kRuns = 2;
+constexpr int kSelRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format, range checked
 
-// Radix passes p0..5 by one wavefront over a candidate list in LDS (no block barriers); same
-// contract as radix_pass. h is a padded 2048-bin histogram owned by this wave.
-__device__ uint64_t wave_radix(const uint64_t* list, uint32_t n, uint32_t need, int p0, uint64_t prefix,
-                               uint64_t mask, uint32_t* h) {
-    const int lane = threadIdx.x & 63;
-    for (int p = p0; p < 6; ++p) {
-        const int shf = kShift[p];
-        const uint64_t dm = ((uint64_t)1 << kWidth[p]) - 1;
-        for (int b = lane; b < kPadBins; b += 64) h[b] = 0u;
-        __threadfence_block();
-        for (uint32_t i = lane; i < n; i += 64) {
-            const uint64_t c = list[i];
-            if (((c ^ prefix) & mask) == 0) atomicAdd(&h[hidx((int)((c >> shf) & dm))], 1u);
-        }
-        __threadfence_block();
-        const Sel r = wave_threshold(h, need);
-        if (r.digit < 0) return 1ull;
-        if (h[hidx(r.digit)] == need - r.above) return prefix | ((uint64_t)r.digit << shf);
-        need -= r.above;
-        prefix |= (uint64_t)r.digit << shf;
-        mask |= dm << shf;
+template <int NT>
+struct SmallShared {
+    static constexpr int kCap = 4 * NT;
+    union {
+        Hist<NT> H;  // register passes
+        struct {
+            uint64_t list[kCap];
+            uint32_t hist[kHistBins];
+        } L;
+    };
+    uint32_t wsum[2][NT / 64];
+    uint32_t t0, kmax, nfin;
+    int digit;
+    uint32_t above;
+    uint64_t T;
+    Sel sel;
+    uint64_t fin[64];
+    uint32_t rk[64];
+};
+
+// inclusive prefix over the 64 lanes of a wavefront with lane moves inside the data-parallel-
+// primitive network: shifts by 1, 2, 4, 8 within each row of 16 lanes, then row 0's last lane
+// into row 1 (and row 2's into row 3), then lane 31 into rows 2 and 3
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
+}
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t v) {
+    v += dpp_or_zero<0x111, 0xF>(v);
+    v += dpp_or_zero<0x112, 0xF>(v);
+    v += dpp_or_zero<0x114, 0xF>(v);
+    v += dpp_or_zero<0x118, 0xF>(v);
+    v += dpp_or_zero<0x142, 0xA>(v);
+    v += dpp_or_zero<0x143, 0xC>(v);
+    return v;
+}
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t v) {
+    v = umax(v, dpp_or_zero<0x111, 0xF>(v));
+    v = umax(v, dpp_or_zero<0x112, 0xF>(v));
+    v = umax(v, dpp_or_zero<0x114, 0xF>(v));
+    v = umax(v, dpp_or_zero<0x118, 0xF>(v));
+    v = umax(v, dpp_or_zero<0x142, 0xA>(v));
+    v = umax(v, dpp_or_zero<0x143, 0xC>(v));
+    return v;
+}
+
+// exclusive prefix of one value per thread over the block, and the block total, with one
+// barrier: wavefront totals go to wsum, and every thread adds up the totals it needs. wsum must
+// not be rewritten before every thread has passed the next barrier (callers alternate buffers).
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint32_t& total) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint32_t v = wave_incl_add(x);
+    if (lane == 63) wsum[w] = v;
+    __syncthreads();
+    uint32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const uint32_t u = wsum[i];
+        tot += u;
+        pre += i < w ? u : 0u;
     }
-    return prefix;
+    total = tot;
+    return pre + v - x;
+}
+
+__device__ __forceinline__ uint64_t list_entry(float v, uint32_t pos) {
+    return ((uint64_t)__float_as_uint(v) << 32) | (uint64_t)(~pos);
+}
+__device__ __forceinline__ uint64_t entry_composite(uint64_t x) {
+    return ((uint64_t)order_key(__uint_as_float((uint32_t)(x >> 32))) << 32) | (x & 0xffffffffull);
+}
+
+template <int NT>
+__device__ __forceinline__ void small_load(const SelectArgs& a, int64_t t, const RowInfo& ri, float (&v)[kRuns][8],
+                                           uint32_t (&pb)[kRuns]) {
+    const int len = (int)ri.len;
+    const int tid = threadIdx.x;
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.vals + t * a.stride), 0, len * 4, kSelRsrcWord3);
+#pragma unroll
+    for (int r = 0; r < kRuns; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            v[r][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, (8 * (tid + r * NT) + e) * 4, 0, 0));
+    if (a.map) {
+        const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.map + t * a.map_stride), 0, ((len + kBlock - 1) / kBlock) * 4, kSelRsrcWord3);
+#pragma unroll
+        for (int r = 0; r < kRuns; ++r)
+            pb[r] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rm, (tid + r * NT) * 4, 0, 0) * (uint32_t)kBlock;
+    } else {
+#pragma unroll
+        for (int r = 0; r < kRuns; ++r) pb[r] = (uint32_t)(8 * (tid + r * NT));
+    }
+#pragma unroll
+    for (int r = 0; r < kRuns; ++r) {
+        const int nvalid = len - 8 * (tid + r * NT);
+        if (nvalid < 8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (e >= nvalid) v[r][e] = -INFINITY;
+        }
+    }
+    if (ri.pin >= 0) {  // the block of the newest position counts as +inf
+        const int pr = (int)(ri.pin >> 3);
+        if (pr % NT == tid) {
+#pragma unroll
+            for (int r = 0; r < kRuns; ++r)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (pr / NT == r && (int)(ri.pin & 7) == e) v[r][e] = INFINITY;
+        }
+    }
+}
+
+// d, above of a 2048-bin histogram (largest d with sum_{b >= d} h[b] >= need) by the whole block;
+// thread tid owns the bins kHistBins - 1 - (B * tid + j), j < B. Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void small_threshold(const uint32_t* h, uint32_t need, SmallShared<NT>& S, uint32_t* wsum) {
+    constexpr int B = kHistBins / NT;
+    uint32_t c[B], s = 0;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+        c[j] = h[kHistBins - 1 - (B * (int)threadIdx.x + j)];
+        s += c[j];
+    }
+    uint32_t tot;
+    const uint32_t ex = block_scan<NT>(s, wsum, tot);
+    if (ex < need && need <= ex + s) {
+        uint32_t acc = ex;
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            if (acc + c[j] >= need) {
+                S.digit = kHistBins - 1 - (B * (int)threadIdx.x + j);
+                S.above = acc;
+                break;
+            }
+            acc += c[j];
+        }
+    }
+    __syncthreads();
 }
 
 template <int NT>
 __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
     constexpr int NW = NT / 64;
-    constexpr int Q = kRowPer * NW / 64;  // (slot, wave) counts per lane in the compaction scan
-    static_assert(Q >= 1 && kRowPer * NW % 64 == 0, "compaction scan needs a whole number of counts per lane");
-    __shared__ Hist<NT> H;
-    __shared__ Sel sel;
-    __shared__ uint32_t woff[kRowPer][NW];
-    __shared__ uint32_t cnt_all;
-    __shared__ uint32_t seg_cnt[NW];
-    __shared__ uint64_t T_sh;
-    // the candidate list reuses the per-wave histogram words, dead after the first pass
-    constexpr int kListCap = sizeof(H.hw) / sizeof(uint64_t) < kListMax ? sizeof(H.hw) / sizeof(uint64_t) : kListMax;
-    uint64_t* list = reinterpret_cast<uint64_t*>(&H.hw[0][0]);
+    constexpr int kCap = SmallShared<NT>::kCap;
+    __shared__ SmallShared<NT> S;
     const int64_t t = blockIdx.x;
     const RowInfo ri = row_info(a, t);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint64_t c[kRowPer];
-    load_composites<kRowPer>(a, t, ri, threadIdx.x, NT, c);
-    auto each = [&](auto&& f) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid == 0) {
+        S.t0 = 0xffffffffu;
+        S.kmax = 0u;
+        S.digit = 0;
+        S.above = 0u;
+        S.T = 1ull;
+    }
+    float v[kRuns][8];
+    uint32_t pb[kRuns];
+    small_load<NT>(a, t, ri, v, pb);
+
+    // 1. T0 and the row maximum key KM (an upper bound: a zero maximum counts as +0)
+    float fm = v[0][0];
 #pragma unroll
-        for (int j = 0; j < kRowPer; ++j) f(c[j]);
-    };
-    uint32_t need = (uint32_t)a.k;
-    uint64_t prefix = 0ull, mask = 0ull, T = ~0ull;
-    if (ri.len > 0 && !radix_pass<NT>(each, 0, need, prefix, mask, T, H, sel)) {
-        // the threshold digit holds H.h[d] candidates; when they fit, they are packed into one LDS
-        // list (per-wave offsets from ballot counts, no atomics) and one wavefront finishes on them
-        const uint32_t ncand = H.h[hidx(sel.digit)];
-        if (ncand <= (uint32_t)kListCap) {
-            const uint64_t below = (1ull << lane) - 1ull;
-            uint64_t m[kRowPer];
-            uint32_t mine = 0;
+    for (int r = 0; r < kRuns; ++r)
 #pragma unroll
-            for (int j = 0; j < kRowPer; ++j) {
-                m[j] = __ballot(c[j] != 0 && ((c[j] ^ prefix) & mask) == 0);
-                mine += (uint32_t)__popcll(m[j]);
-            }
-            if (lane == 0) seg_cnt[w] = mine;
-            __syncthreads();
-            uint32_t base = 0;
-            for (int sg = 0; sg < w; ++sg) base += seg_cnt[sg];
-#pragma unroll
-            for (int j = 0; j < kRowPer; ++j) {
-                if ((m[j] >> lane) & 1ull) list[base + (uint32_t)__popcll(m[j] & below)] = c[j];
-                base += (uint32_t)__popcll(m[j]);
-            }
-            __syncthreads();
-            if (threadIdx.x < 64) {
-                const uint64_t r = wave_radix(list, ncand, need, 1, prefix, mask, H.h);
-                if (threadIdx.x == 0) T_sh = r;
-            }
-            __syncthreads();
-            T = T_sh;
-        } else {
-            for (int p = 1; p < 6; ++p)
-                if (radix_pass<NT>(each, p, need, prefix, mask, T, H, sel)) break;
+        for (int e = 0; e < 8; ++e) fm = fmaxf(fm, v[r][e]);
+    const uint32_t kfm = order_key(fm);
+    const uint32_t tm_lo = eligible(kfm) ? kfm : 0u;
+    const uint32_t tm_hi = tm_lo == 0x7fffffffu ? 0x80000000u : tm_lo;
+    const uint32_t R = ((uint32_t)a.k + NW - 1) / NW;
+    uint32_t t0w = 0u;
+    if (R <= 64) {  // the top 16 key bits suffice for a lower bound
+        for (int b = 31; b >= 16; --b) {
+            const uint32_t tr = t0w | (1u << b);
+            if ((uint32_t)__popcll(__ballot(tm_lo >= tr)) >= R) t0w = tr;
         }
     }
-    // ordered compaction: slot order (j, wave, lane)
-    uint64_t m[kRowPer];
-#pragma unroll
-    for (int j = 0; j < kRowPer; ++j) {
-        m[j] = __ballot(c[j] != 0 && c[j] >= T);
-        if (lane == 0) woff[j][w] = (uint32_t)__popcll(m[j]);
+    const uint32_t mw = wave_incl_max(tm_hi);  // lane 63: the wavefront maximum
+    __syncthreads();
+    if (lane == 63) {
+        atomicMin(&S.t0, t0w);
+        atomicMax(&S.kmax, mw);
     }
     __syncthreads();
-    if (threadIdx.x < 64) {  // exclusive scan of the kRowPer * NW (j, wave) counts, Q per lane
-        uint32_t e[Q], s = 0;
+    const uint32_t T0 = S.t0, KM = S.kmax;
+    const float fT = T0 ? key_value(T0) : -__FLT_MAX__;  // v >= fT: every value with key >= T0 (and -0 at +0)
+
+    // 2. candidates: counts per run, packed, one scan gives slot-order offsets
+    uint32_t cr[kRuns];
+#pragma unroll
+    for (int r = 0; r < kRuns; ++r) {
+        cr[r] = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cr[r] += v[r][e] >= fT ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t ex = block_scan<NT>(cr[0] | (cr[1] << 16), S.wsum[0], tot);
+    const uint32_t C = (tot & 0xffffu) + (tot >> 16);
+    const uint32_t k = (uint32_t)a.k;
+    uint64_t T = 1ull;  // every candidate
+    uint32_t cnt;
+    if (C <= (uint32_t)kCap) {
+        uint32_t o[kRuns] = {ex & 0xffffu, (tot & 0xffffu) + (ex >> 16)};
+#pragma unroll
+        for (int r = 0; r < kRuns; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (v[r][e] >= fT) S.L.list[o[r]++] = list_entry(v[r][e], pb[r] + (uint32_t)e);
+        __syncthreads();
+        // 3. radix passes over the list
+        if (C > k) {
+            const uint32_t dk = T0 ^ KM;
+            int hi = dk ? 63 - __clz(dk) : 31;
+            uint64_t mask = hi >= 63 ? 0ull : ~((1ull << (hi + 1)) - 1ull);
+            uint64_t prefix = ((uint64_t)T0 << 32) & mask;
+            uint32_t need = k;
+            int sb = 1;  // scan buffer
+            for (;;) {
+                const int width = hi + 1 < 11 ? hi + 1 : 11;
+                const int lo = hi - width + 1;
+                const uint64_t dm = (1ull << width) - 1ull;
+                __syncthreads();  // readers of the previous histogram are done
+                for (int b = tid; b < kHistBins; b += NT) S.L.hist[b] = 0u;
+                __syncthreads();
+                for (uint32_t i = tid; i < C; i += NT) {
+                    const uint64_t x = entry_composite(S.L.list[i]);
+                    if (((x ^ prefix) & mask) == 0) atomicAdd(&S.L.hist[(x >> lo) & dm], 1u);
+                }
+                __syncthreads();
+                small_threshold<NT>(S.L.hist, need, S, S.wsum[sb]);
+                sb ^= 1;
+                const int d = S.digit;
+                const uint32_t above = S.above;
+                const uint32_t on = S.L.hist[d];
+                if (on == need - above) {
+                    T = prefix | ((uint64_t)d << lo);
+                    break;
+                }
+                need -= above;
+                prefix |= (uint64_t)d << lo;
+                mask |= dm << lo;
+                hi = lo - 1;
+                if (on <= 64 || hi < 0) {
+                    // the few elements on the digit, ranked against each other
+                    if (tid == 0) S.nfin = 0u;
+                    if (tid < 64) S.rk[tid] = 0u;
+                    __syncthreads();
+                    for (uint32_t i = tid; i < C; i += NT) {
+                        const uint64_t x = entry_composite(S.L.list[i]);
+                        if (((x ^ prefix) & mask) == 0) {
+                            const uint32_t f = atomicAdd(&S.nfin, 1u);
+                            if (f < 64u) S.fin[f] = x;
+                        }
+                    }
+                    __syncthreads();
+                    const uint32_t nf = S.nfin < 64u ? S.nfin : 64u;
+                    constexpr int per = (64 + NW - 1) / NW;
+                    if ((uint32_t)lane < nf) {
+                        const uint64_t xi = S.fin[lane];
+                        uint32_t rank = 0;
+#pragma unroll
+                        for (int jj = 0; jj < per; ++jj) {
+                            const uint32_t j = (uint32_t)(w * per + jj);
+                            if (j < nf && S.fin[j] > xi) ++rank;
+                        }
+                        if (rank) atomicAdd(&S.rk[lane], rank);
+                    }
+                    __syncthreads();
+                    if ((uint32_t)tid < nf && S.rk[tid] == need - 1) S.T = S.fin[tid];
+                    __syncthreads();
+                    T = S.T;
+                    break;
+                }
+            }
+        }
+        // 4. list entries >= T, in list order: thread tid takes entries [Q * tid, Q * tid + Q)
+        constexpr int Q = kCap / NT;
+        uint64_t x[Q];
+        uint32_t wm = 0, c = 0;
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-            const int idx = Q * lane + q;
-            e[q] = woff[idx / NW][idx % NW];
-            s += e[q];
+            const uint32_t i = (uint32_t)(Q * tid + q);
+            x[q] = i < C ? entry_composite(S.L.list[i]) : 0ull;
+            const bool win = i < C && x[q] >= T;
+            wm |= (win ? 1u : 0u) << q;
+            c += win ? 1u : 0u;
         }
-        uint32_t u = s;
+        __syncthreads();  // every scan buffer is free again
+        uint32_t slot = block_scan<NT>(c, S.wsum[0], cnt);
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_up(u, off);
-            if (lane >= off) u += y;
-        }
-        uint32_t run = u - s;
+        for (int q = 0; q < Q; ++q)
+            if ((wm >> q) & 1u) {
+                if (slot < k) write_one(a, t, (int)slot, x[q]);
+                ++slot;
+            }
+    } else {
+        // register passes over the composites
+        auto each = [&](auto&& f) {
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const int idx = Q * lane + q;
-            woff[idx / NW][idx % NW] = run;
-            run += e[q];
-        }
-        if (lane == 63) cnt_all = u;
+            for (int r = 0; r < kRuns; ++r)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t kk = order_key(v[r][e]);
+                    f(eligible(kk) ? composite(kk, pb[r] + (uint32_t)e) : 0ull);
+                }
+        };
+        uint32_t need = k;
+        uint64_t prefix = 0ull, mask = 0ull;
+        for (int p = 0; p < 6; ++p)
+            if (radix_pass<NT>(each, p, need, prefix, mask, T, S.H, S.sel)) break;
+        uint32_t wr[kRuns] = {0, 0};
+#pragma unroll
+        for (int r = 0; r < kRuns; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t kk = order_key(v[r][e]);
+                if (eligible(kk) && composite(kk, pb[r] + (uint32_t)e) >= T) wr[r] |= 1u << e;
+            }
+        __syncthreads();
+        uint32_t tot2;
+        const uint32_t ex2 = block_scan<NT>((uint32_t)__popc(wr[0]) | ((uint32_t)__popc(wr[1]) << 16), S.wsum[0],
+                                            tot2);
+        uint32_t o[kRuns] = {ex2 & 0xffffu, (tot2 & 0xffffu) + (ex2 >> 16)};
+        cnt = (tot2 & 0xffffu) + (tot2 >> 16);
+#pragma unroll
+        for (int r = 0; r < kRuns; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if ((wr[r] >> e) & 1u) {
+                    if (o[r] < k) write_one(a, t, (int)o[r], composite(order_key(v[r][e]), pb[r] + (uint32_t)e));
+                    ++o[r];
+                }
     }
-    __syncthreads();
-    const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-    for (int j = 0; j < kRowPer; ++j) {
-        if ((m[j] >> lane) & 1ull) {
-            const uint32_t slot = woff[j][w] + (uint32_t)__popcll(m[j] & below);
-            if (slot < (uint32_t)a.k) write_one(a, t, (int)slot, c[j]);
-        }
-    }
-    const uint32_t cnt = cnt_all < (uint32_t)a.k ? cnt_all : (uint32_t)a.k;
-    write_pad(a, t, cnt);
+    write_pad(a, t, cnt < k ? cnt : k);
 }
 
 // ---------------------------------------------------------------- longer rows
@@ -681,10 +906,13 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
     if (a.nq <= 0) return hipSuccess;
     const int64_t cap = row_cap(a);
     if (cap <= kSmallRow) {
+        // the block holds 16 values per thread, and T0 needs k <= NT to bound the candidates
         const dim3 grid((unsigned)a.nq);
-        if (cap <= 256 * kRowPer)
+        const int64_t per_thread = (cap + 8 * kRuns - 1) / (8 * kRuns);
+        const int64_t nt = per_thread > a.k ? per_thread : a.k;
+        if (nt <= 256)
             hipLaunchKernelGGL(select_small_kernel<256>, grid, dim3(256), 0, stream, a);
-        else if (cap <= 512 * kRowPer)
+        else if (nt <= 512)
             hipLaunchKernelGGL(select_small_kernel<512>, grid, dim3(512), 0, stream, a);
         else
             hipLaunchKernelGGL(select_small_kernel<1024>, grid, dim3(1024), 0, stream, a);
