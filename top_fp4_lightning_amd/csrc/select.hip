@@ -2,41 +2,26 @@
 //
 // Every element gets a unique 64-bit composite c = (key << 32) | ~pos, where key is the fp32
 // bit pattern mapped to an order-preserving uint32 and pos the element's reported index; -inf
-// and NaN get c = 0 (never selected). The top k are exactly the elements with c >= T, where T
-// is found by radix passes of 11 bits over the composite (most significant digit first): each
-// pass histograms the digit among elements matching the digits fixed so far, takes the digit
-// where the count from the top reaches the number still needed, and stops as soon as every
-// element on that digit is needed. Histograms are private per wavefront (two 16-bit counters per
-// LDS word); the summed histogram is stored with one pad word per 32 bins so that a lane can
-// read its own 32 consecutive bins without bank conflicts.
+// and NaN never enter the selection. The top k are exactly the elements with c >= T. T is found
+// by radix passes of 11 bits over the composites of a short candidate list: a lower bound of the
+// k-th key, taken from wavefront maxima, admits a few percent of a row as candidates (details
+// above the candidate filter below).
 //
 // The winners are written in ascending position order (the natural order for gathering the
-// selected keys afterwards), with no sort on the hot paths:
-//  - rows of at most 16384 values: one block per row (256, 512 or 1024 threads by row capacity),
-//    16 composites per thread in registers (one launch); the first radix pass runs over the whole row, the remaining ones on
-//    the elements of the threshold digit only (copied to LDS, one wavefront, no block barriers);
-//    winners are compacted in slot order with wavefront ballots, which is
-//    position order when the optional block map is ascending (as the pool and this function
-//    produce);
+// selected keys afterwards):
+//  - rows of at most 16384 values: one block per row (256, 512 or 1024 threads), 16 values per
+//    thread in registers (one launch); the candidates sit in LDS in slot order and the winners
+//    are written in that order, which is position order when the optional block map is
+//    ascending (as the pool and this function produce);
 //  - longer rows (candidate pool over 2^17 block maxima, full score rows): three launches over
-//    chunks of 4096 values, ordered by kernel boundaries (no cross-block fences):
-//      hist   - chunk histogram of the top 11 key bits, added to the row histogram (atomics);
-//      filter - every chunk derives the threshold digit from the row histogram; values above it
-//               are certain winners, values on it candidates; both are appended to workspace
-//               lists (one reservation atomic per chunk and list);
-//      finish - one block per row finishes the radix passes over the candidates, orders the
-//               winners (LDS bitmap for pool block ids, else a bitonic sort by position), writes
-//               them and clears the row's histogram and counters for the next call.
+//    chunks of 4096 values (bound, collect, finish; ordered by kernel boundaries, no cross-block
+//    fences or waits); the finishing block orders the winners by position.
 #include "internal.h"
 
 namespace fp4idx {
 namespace {
 
 constexpr int kSmallRow = 16384;
-constexpr int kPer = 16;  // values per thread
-constexpr int kLargeThreads = 256;
-constexpr int kChunk = kLargeThreads * kPer;
-constexpr int kFinishThreads = 1024;
 constexpr int kPadBins = kHistBins + kHistBins / 32;
 constexpr int64_t kBitmapMax = (int64_t)1 << 18;  // pool rows up to this many blocks use the bitmap
 
@@ -80,45 +65,6 @@ __device__ __forceinline__ RowInfo row_info(const SelectArgs& a, int64_t t) {
         ri.pin = -1;
     }
     return ri;
-}
-
-// Composites of elements base + j * stride, j < E (0 if absent or not eligible). All loads are
-// issued before any is used (clamped in-bounds indices, masked afterwards).
-template <int E>
-__device__ __forceinline__ void load_composites(const SelectArgs& a, int64_t t, const RowInfo& ri, int64_t base,
-                                                int64_t stride, uint64_t (&c)[E]) {
-    if (ri.len <= 0) {
-#pragma unroll
-        for (int j = 0; j < E; ++j) c[j] = 0ull;
-        return;
-    }
-    float v[E];
-    int32_t m[E];
-    const float* row = a.vals + t * a.stride;
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-        const int64_t i = base + j * stride;
-        v[j] = row[i < ri.len ? i : ri.len - 1];
-    }
-    if (a.map) {
-        const int32_t* mrow = a.map + t * a.map_stride;
-#pragma unroll
-        for (int j = 0; j < E; ++j) {
-            const int64_t i = base + j * stride;
-            m[j] = mrow[(i < ri.len ? i : ri.len - 1) >> 3];
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-        const int64_t i = base + j * stride;
-        const uint32_t k = i == ri.pin ? 0xff800000u : order_key(v[j]);  // the pinned block is +inf
-        if (i >= ri.len || !eligible(k)) {
-            c[j] = 0ull;
-        } else {
-            const uint32_t pos = a.map ? (uint32_t)(m[j] * kBlock + (int32_t)(i & 7)) : (uint32_t)i;
-            c[j] = composite(k, pos);
-        }
-    }
 }
 
 __device__ __constant__ int kShift[6] = {53, 42, 31, 20, 9, 0};
@@ -236,36 +182,6 @@ __device__ bool radix_pass(Each each, int p, uint32_t& need, uint64_t& prefix, u
     return false;
 }
 
-// exclusive scan of one value per thread over the block (NT threads); returns the prefix,
-// sets *total
-template <int NT>
-__device__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* wsum, uint32_t* total) {
-    constexpr int NW = NT / 64;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint32_t v = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(v, off);
-        if (lane >= off) v += y;
-    }
-    __syncthreads();
-    if (lane == 63) wsum[w] = v;
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        const uint32_t s = lane < NW ? wsum[lane] : 0u;
-        uint32_t u = s;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_up(u, off);
-            if (lane >= off) u += y;
-        }
-        if (lane < NW) wsum[lane] = u - s;
-        if (lane == 63) *total = u;
-    }
-    __syncthreads();
-    return wsum[w] + v - x;
-}
-
 __device__ __forceinline__ uint64_t cmpx(uint64_t v, uint64_t p, bool keep_min) {
     return keep_min ? (v < p ? v : p) : (v < p ? p : v);
 }
@@ -337,44 +253,24 @@ __device__ __forceinline__ void write_pad(const SelectArgs& a, int64_t t, uint32
     if (a.out_count && threadIdx.x == 0) a.out_count[t] = (int32_t)cnt;
 }
 
-// ---------------------------------------------------------------- rows of <= 16 * NT values
-// One block per row. Thread tid holds the values of slots 8 * (tid + r * NT) + e (run r < 2,
-// e < 8) in registers (-inf past the row, +inf for the pinned block) and the position of each
-// run's first slot. Work per value is a handful of instructions; everything else runs on a short
-// candidate list:
-//  1. A lower bound T0 of the k-th largest key: each wavefront takes the R-th largest of its
-//     lanes' maxima, R = ceil(k / wavefronts), so at least R lanes of every wavefront (k values
-//     in all) hold a value at or above the smallest of these.
-//  2. The values at or above T0 (a few percent of a row) go to an LDS list in slot order, as
+// ---------------------------------------------------------------- candidate filter and list radix
+// Rows are read as runs of 8 consecutive slots: in a block of NT threads, thread tid holds the
+// values of slots c0 + 8 * (tid + r * NT) + e (run r < 2, e < 8) as floats in registers, -inf
+// past the row and +inf for the pinned block, plus the position of each run's first slot (block
+// map entry * 8, or the slot itself). Work per value is a handful of instructions:
+//  1. A lower bound T0 of the k-th largest key. A wavefront with at least R eligible lanes
+//     contributes the R-th largest of its lanes' maxima; when the contributing wavefronts number
+//     at least k / R, at least k values lie at or above the smallest contribution, T0.
+//     (Without enough contributions T0 = 0 and every eligible value is a candidate.)
+//  2. The values at or above T0 (a few percent of a row) become candidates, stored as
 //     (value bits, ~position).
-//  3. Radix passes over the list find T: the first digit starts below the bits that T0 and the
-//     row maximum share; passes stop when the threshold digit holds exactly the elements still
-//     needed, or at most 64 of them, which are then ranked against each other in parallel.
-//  4. The list entries >= T are written in list order.
-// When R > 64 or the candidates overflow the list, the radix passes run over the registers
-// (wave-private histograms) and the winners are compacted from the registers.
+//  3. Radix passes over the candidates find T: the first digit starts below the bits that T0 and
+//     the row maximum share; passes stop when the threshold digit holds exactly the elements
+//     still needed, or at most 64 of them, which are then ranked against each other in parallel.
+//  4. The candidates >= T are the winners.
 constexpr int kRuns = 2;
+constexpr int kRunSlots = 8 * kRuns;  // values per thread
 constexpr int kSelRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format, range checked
-
-template <int NT>
-struct SmallShared {
-    static constexpr int kCap = 4 * NT;
-    union {
-        Hist<NT> H;  // register passes
-        struct {
-            uint64_t list[kCap];
-            uint32_t hist[kHistBins];
-        } L;
-    };
-    uint32_t wsum[2][NT / 64];
-    uint32_t t0, kmax, nfin;
-    int digit;
-    uint32_t above;
-    uint64_t T;
-    Sel sel;
-    uint64_t fin[64];
-    uint32_t rk[64];
-};
 
 // inclusive prefix over the 64 lanes of a wavefront with lane moves inside the data-parallel-
 // primitive network: shifts by 1, 2, 4, 8 within each row of 16 lanes, then row 0's last lane
@@ -432,12 +328,13 @@ __device__ __forceinline__ uint64_t entry_composite(uint64_t x) {
 }
 
 template <int NT>
-__device__ __forceinline__ void small_load(const SelectArgs& a, int64_t t, const RowInfo& ri, float (&v)[kRuns][8],
-                                           uint32_t (&pb)[kRuns]) {
-    const int len = (int)ri.len;
+__device__ __forceinline__ void chunk_load(const SelectArgs& a, int64_t t, const RowInfo& ri, int64_t c0,
+                                           float (&v)[kRuns][8], uint32_t (&pb)[kRuns]) {
+    const int64_t rem64 = ri.len - c0;
+    const int rem = rem64 < (int64_t)(kRunSlots * NT) ? (int)rem64 : kRunSlots * NT;
     const int tid = threadIdx.x;
     const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(a.vals + t * a.stride), 0, len * 4, kSelRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.vals + t * a.stride + c0), 0, rem * 4, kSelRsrcWord3);
 #pragma unroll
     for (int r = 0; r < kRuns; ++r)
 #pragma unroll
@@ -445,62 +342,226 @@ __device__ __forceinline__ void small_load(const SelectArgs& a, int64_t t, const
             v[r][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, (8 * (tid + r * NT) + e) * 4, 0, 0));
     if (a.map) {
         const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(a.map + t * a.map_stride), 0, ((len + kBlock - 1) / kBlock) * 4, kSelRsrcWord3);
+            (void*)(a.map + t * a.map_stride + c0 / kBlock), 0, ((rem + kBlock - 1) / kBlock) * 4, kSelRsrcWord3);
 #pragma unroll
         for (int r = 0; r < kRuns; ++r)
             pb[r] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rm, (tid + r * NT) * 4, 0, 0) * (uint32_t)kBlock;
     } else {
 #pragma unroll
-        for (int r = 0; r < kRuns; ++r) pb[r] = (uint32_t)(8 * (tid + r * NT));
+        for (int r = 0; r < kRuns; ++r) pb[r] = (uint32_t)(c0 + 8 * (tid + r * NT));
     }
 #pragma unroll
     for (int r = 0; r < kRuns; ++r) {
-        const int nvalid = len - 8 * (tid + r * NT);
+        const int nvalid = rem - 8 * (tid + r * NT);
         if (nvalid < 8) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 if (e >= nvalid) v[r][e] = -INFINITY;
         }
     }
-    if (ri.pin >= 0) {  // the block of the newest position counts as +inf
-        const int pr = (int)(ri.pin >> 3);
+    if (ri.pin >= c0 && ri.pin < c0 + rem) {  // the block of the newest position counts as +inf
+        const int p = (int)(ri.pin - c0);
+        const int pr = p >> 3;
         if (pr % NT == tid) {
 #pragma unroll
             for (int r = 0; r < kRuns; ++r)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    if (pr / NT == r && (int)(ri.pin & 7) == e) v[r][e] = INFINITY;
+                    if (pr / NT == r && (p & 7) == e) v[r][e] = INFINITY;
         }
     }
 }
 
-// d, above of a 2048-bin histogram (largest d with sum_{b >= d} h[b] >= need) by the whole block;
-// thread tid owns the bins kHistBins - 1 - (B * tid + j), j < B. Ends with a barrier.
-template <int NT>
-__device__ __forceinline__ void small_threshold(const uint32_t* h, uint32_t need, SmallShared<NT>& S, uint32_t* wsum) {
-    constexpr int B = kHistBins / NT;
-    uint32_t c[B], s = 0;
+// key of the thread's largest value, a zero maximum counted as -0 (a lower bound); 0 when the
+// thread holds no eligible value
+__device__ __forceinline__ uint32_t lane_max(const float (&v)[kRuns][8]) {
+    float fm = v[0][0];
 #pragma unroll
-    for (int j = 0; j < B; ++j) {
-        c[j] = h[kHistBins - 1 - (B * (int)threadIdx.x + j)];
-        s += c[j];
+    for (int r = 0; r < kRuns; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fm = fmaxf(fm, v[r][e]);
+    const uint32_t k = order_key(fm);
+    return eligible(k) ? k : 0u;
+}
+
+// the R-th largest lo key of the wavefront's lanes, to its top 16 bits (0 when fewer than R
+// lanes hold an eligible value)
+__device__ __forceinline__ uint32_t wave_rth(uint32_t lo, uint32_t R) {
+    uint32_t t = 0u;
+    for (int b = 31; b >= 16; --b) {
+        const uint32_t tr = t | (1u << b);
+        if ((uint32_t)__popcll(__ballot(lo >= tr)) >= R) t = tr;
     }
-    uint32_t tot;
-    const uint32_t ex = block_scan<NT>(s, wsum, tot);
-    if (ex < need && need <= ex + s) {
-        uint32_t acc = ex;
+    return t;
+}
+
+// R for a row of `waves` wavefronts of which at least `waves / share` contribute
+__device__ __forceinline__ uint32_t bound_rank(uint32_t k, int64_t waves, int share) {
+    const int64_t r = waves > 0 ? ((int64_t)share * k + waves - 1) / waves : 64;
+    return (uint32_t)(r < 1 ? 1 : (r > 64 ? 64 : r));
+}
+
+template <int NT>
+struct RadixShared {
+    uint32_t wsum[2][NT / 64];
+    uint32_t red[2][NT / 64];
+    int digit;
+    uint32_t above, nfin;
+    uint64_t T;
+    uint64_t fin[64];
+    uint32_t rk[64];
+};
+
+constexpr uint32_t kInfKey = 0xff800000u;  // order key of +inf
+
+// T for the candidates L[0 .. C) (C > k, at least k of them with keys >= T0); hist is a 2048-bin
+// scratch histogram. Called by the whole block; contains barriers. +inf entries (the pinned
+// block, +inf values) are counted first and kept out of the passes, so that the first digit
+// starts below the bits shared by T0 and the largest finite key.
+template <int NT>
+__device__ uint64_t list_radix(const uint64_t* L, uint32_t C, uint32_t k, uint32_t T0, uint32_t* hist,
+                               RadixShared<NT>& S) {
+    constexpr int NW = NT / 64;
+    constexpr int B = kHistBins / NT;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid == 0) {
+        S.digit = 0;
+        S.above = 0u;
+        S.T = 1ull;
+    }
+    uint32_t km = 0u, ni = 0u;
+    for (uint32_t i = tid; i < C; i += NT) {
+        const uint32_t kk = order_key(__uint_as_float((uint32_t)(L[i] >> 32)));
+        if (kk >= kInfKey)
+            ++ni;
+        else
+            km = kk > km ? kk : km;
+    }
+    km = wave_incl_max(km);
+    ni = wave_incl_add(ni);
+    if (lane == 63) {
+        S.red[0][w] = km;
+        S.red[1][w] = ni;
+    }
+    __syncthreads();
+    km = 0u;
+    ni = 0u;
 #pragma unroll
-        for (int j = 0; j < B; ++j) {
-            if (acc + c[j] >= need) {
-                S.digit = kHistBins - 1 - (B * (int)threadIdx.x + j);
-                S.above = acc;
-                break;
+    for (int i = 0; i < NW; ++i) {
+        km = S.red[0][i] > km ? S.red[0][i] : km;
+        ni += S.red[1][i];
+    }
+    uint32_t need = k;
+    int hi;
+    uint64_t mask, prefix, lim;
+    if (ni >= need) {  // the threshold lies among the +inf entries: positions decide
+        hi = 31;
+        mask = 0xffffffff00000000ull;
+        prefix = (uint64_t)kInfKey << 32;
+        lim = ~0ull;
+    } else {
+        need -= ni;
+        const uint32_t dk = T0 ^ km;
+        hi = dk ? 63 - __clz(dk) : 31;
+        mask = hi >= 63 ? 0ull : ~((1ull << (hi + 1)) - 1ull);
+        prefix = ((uint64_t)T0 << 32) & mask;
+        lim = (uint64_t)kInfKey << 32;
+    }
+    int sb = 0;
+    for (;;) {
+        const int width = hi + 1 < 11 ? hi + 1 : 11;
+        const int lo = hi - width + 1;
+        const uint64_t dm = (1ull << width) - 1ull;
+        __syncthreads();  // readers of the previous histogram are done
+        for (int b = tid; b < kHistBins; b += NT) hist[b] = 0u;
+        __syncthreads();
+        for (uint32_t i = tid; i < C; i += NT) {
+            const uint64_t x = entry_composite(L[i]);
+            if (((x ^ prefix) & mask) == 0 && x < lim) atomicAdd(&hist[(x >> lo) & dm], 1u);
+        }
+        __syncthreads();
+        {  // threshold digit: thread tid owns bins kHistBins - 1 - (B * tid + j), j < B
+            uint32_t c[B], sum = 0;
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                c[j] = hist[kHistBins - 1 - (B * tid + j)];
+                sum += c[j];
             }
-            acc += c[j];
+            uint32_t tot;
+            const uint32_t ex = block_scan<NT>(sum, S.wsum[sb], tot);
+            sb ^= 1;
+            if (ex < need && need <= ex + sum) {
+                uint32_t acc = ex;
+#pragma unroll
+                for (int j = 0; j < B; ++j) {
+                    if (acc + c[j] >= need) {
+                        S.digit = kHistBins - 1 - (B * tid + j);
+                        S.above = acc;
+                        break;
+                    }
+                    acc += c[j];
+                }
+            }
+            __syncthreads();
+        }
+        const int d = S.digit;
+        const uint32_t above = S.above;
+        const uint32_t on = hist[d];
+        if (on == need - above) return prefix | ((uint64_t)d << lo);
+        need -= above;
+        prefix |= (uint64_t)d << lo;
+        mask |= dm << lo;
+        hi = lo - 1;
+        if (on <= 64 || hi < 0) break;
+    }
+    // the few elements on the digit, ranked against each other
+    if (tid == 0) S.nfin = 0u;
+    if (tid < 64) S.rk[tid] = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < C; i += NT) {
+        const uint64_t x = entry_composite(L[i]);
+        if (((x ^ prefix) & mask) == 0 && x < lim) {
+            const uint32_t f = atomicAdd(&S.nfin, 1u);
+            if (f < 64u) S.fin[f] = x;
         }
     }
     __syncthreads();
+    const uint32_t nf = S.nfin < 64u ? S.nfin : 64u;
+    constexpr int per = (64 + NW - 1) / NW;
+    if ((uint32_t)lane < nf) {
+        const uint64_t xi = S.fin[lane];
+        uint32_t rank = 0;
+#pragma unroll
+        for (int jj = 0; jj < per; ++jj) {
+            const uint32_t j = (uint32_t)(w * per + jj);
+            if (j < nf && S.fin[j] > xi) ++rank;
+        }
+        if (rank) atomicAdd(&S.rk[lane], rank);
+    }
+    __syncthreads();
+    if ((uint32_t)tid < nf && S.rk[tid] == need - 1) S.T = S.fin[tid];
+    __syncthreads();
+    return S.T;
 }
+
+// ---------------------------------------------------------------- rows of <= 16 * NT values
+// One block per row, all four steps in registers and LDS. When R > 64 would be needed or the
+// candidates overflow the list, the radix passes run over the registers instead (wave-private
+// histograms) and the winners are compacted from the registers.
+template <int NT>
+struct SmallShared {
+    static constexpr int kCap = 4 * NT;
+    union {
+        Hist<NT> H;  // register passes
+        struct {
+            uint64_t list[kCap];
+            uint32_t hist[kHistBins];
+        } L;
+    };
+    RadixShared<NT> R;
+    uint32_t t0;
+    Sel sel;
+};
 
 template <int NT>
 __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
@@ -509,43 +570,19 @@ __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
     __shared__ SmallShared<NT> S;
     const int64_t t = blockIdx.x;
     const RowInfo ri = row_info(a, t);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if (tid == 0) {
-        S.t0 = 0xffffffffu;
-        S.kmax = 0u;
-        S.digit = 0;
-        S.above = 0u;
-        S.T = 1ull;
-    }
+    const int tid = threadIdx.x, lane = tid & 63;
+    if (tid == 0) S.t0 = 0xffffffffu;
     float v[kRuns][8];
     uint32_t pb[kRuns];
-    small_load<NT>(a, t, ri, v, pb);
+    chunk_load<NT>(a, t, ri, 0, v, pb);
 
-    // 1. T0 and the row maximum key KM (an upper bound: a zero maximum counts as +0)
-    float fm = v[0][0];
-#pragma unroll
-    for (int r = 0; r < kRuns; ++r)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) fm = fmaxf(fm, v[r][e]);
-    const uint32_t kfm = order_key(fm);
-    const uint32_t tm_lo = eligible(kfm) ? kfm : 0u;
-    const uint32_t tm_hi = tm_lo == 0x7fffffffu ? 0x80000000u : tm_lo;
+    // 1. T0 (every wavefront must contribute here)
     const uint32_t R = ((uint32_t)a.k + NW - 1) / NW;
-    uint32_t t0w = 0u;
-    if (R <= 64) {  // the top 16 key bits suffice for a lower bound
-        for (int b = 31; b >= 16; --b) {
-            const uint32_t tr = t0w | (1u << b);
-            if ((uint32_t)__popcll(__ballot(tm_lo >= tr)) >= R) t0w = tr;
-        }
-    }
-    const uint32_t mw = wave_incl_max(tm_hi);  // lane 63: the wavefront maximum
+    const uint32_t t0w = R <= 64 ? wave_rth(lane_max(v), R) : 0u;
     __syncthreads();
-    if (lane == 63) {
-        atomicMin(&S.t0, t0w);
-        atomicMax(&S.kmax, mw);
-    }
+    if (lane == 0) atomicMin(&S.t0, t0w);
     __syncthreads();
-    const uint32_t T0 = S.t0, KM = S.kmax;
+    const uint32_t T0 = S.t0;
     const float fT = T0 ? key_value(T0) : -__FLT_MAX__;  // v >= fT: every value with key >= T0 (and -0 at +0)
 
     // 2. candidates: counts per run, packed, one scan gives slot-order offsets
@@ -557,7 +594,7 @@ __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
         for (int e = 0; e < 8; ++e) cr[r] += v[r][e] >= fT ? 1u : 0u;
     }
     uint32_t tot;
-    const uint32_t ex = block_scan<NT>(cr[0] | (cr[1] << 16), S.wsum[0], tot);
+    const uint32_t ex = block_scan<NT>(cr[0] | (cr[1] << 16), S.R.wsum[0], tot);
     const uint32_t C = (tot & 0xffffu) + (tot >> 16);
     const uint32_t k = (uint32_t)a.k;
     uint64_t T = 1ull;  // every candidate
@@ -571,71 +608,7 @@ __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
                 if (v[r][e] >= fT) S.L.list[o[r]++] = list_entry(v[r][e], pb[r] + (uint32_t)e);
         __syncthreads();
         // 3. radix passes over the list
-        if (C > k) {
-            const uint32_t dk = T0 ^ KM;
-            int hi = dk ? 63 - __clz(dk) : 31;
-            uint64_t mask = hi >= 63 ? 0ull : ~((1ull << (hi + 1)) - 1ull);
-            uint64_t prefix = ((uint64_t)T0 << 32) & mask;
-            uint32_t need = k;
-            int sb = 1;  // scan buffer
-            for (;;) {
-                const int width = hi + 1 < 11 ? hi + 1 : 11;
-                const int lo = hi - width + 1;
-                const uint64_t dm = (1ull << width) - 1ull;
-                __syncthreads();  // readers of the previous histogram are done
-                for (int b = tid; b < kHistBins; b += NT) S.L.hist[b] = 0u;
-                __syncthreads();
-                for (uint32_t i = tid; i < C; i += NT) {
-                    const uint64_t x = entry_composite(S.L.list[i]);
-                    if (((x ^ prefix) & mask) == 0) atomicAdd(&S.L.hist[(x >> lo) & dm], 1u);
-                }
-                __syncthreads();
-                small_threshold<NT>(S.L.hist, need, S, S.wsum[sb]);
-                sb ^= 1;
-                const int d = S.digit;
-                const uint32_t above = S.above;
-                const uint32_t on = S.L.hist[d];
-                if (on == need - above) {
-                    T = prefix | ((uint64_t)d << lo);
-                    break;
-                }
-                need -= above;
-                prefix |= (uint64_t)d << lo;
-                mask |= dm << lo;
-                hi = lo - 1;
-                if (on <= 64 || hi < 0) {
-                    // the few elements on the digit, ranked against each other
-                    if (tid == 0) S.nfin = 0u;
-                    if (tid < 64) S.rk[tid] = 0u;
-                    __syncthreads();
-                    for (uint32_t i = tid; i < C; i += NT) {
-                        const uint64_t x = entry_composite(S.L.list[i]);
-                        if (((x ^ prefix) & mask) == 0) {
-                            const uint32_t f = atomicAdd(&S.nfin, 1u);
-                            if (f < 64u) S.fin[f] = x;
-                        }
-                    }
-                    __syncthreads();
-                    const uint32_t nf = S.nfin < 64u ? S.nfin : 64u;
-                    constexpr int per = (64 + NW - 1) / NW;
-                    if ((uint32_t)lane < nf) {
-                        const uint64_t xi = S.fin[lane];
-                        uint32_t rank = 0;
-#pragma unroll
-                        for (int jj = 0; jj < per; ++jj) {
-                            const uint32_t j = (uint32_t)(w * per + jj);
-                            if (j < nf && S.fin[j] > xi) ++rank;
-                        }
-                        if (rank) atomicAdd(&S.rk[lane], rank);
-                    }
-                    __syncthreads();
-                    if ((uint32_t)tid < nf && S.rk[tid] == need - 1) S.T = S.fin[tid];
-                    __syncthreads();
-                    T = S.T;
-                    break;
-                }
-            }
-        }
+        if (C > k) T = list_radix<NT>(S.L.list, C, k, T0, S.L.hist, S.R);
         // 4. list entries >= T, in list order: thread tid takes entries [Q * tid, Q * tid + Q)
         constexpr int Q = kCap / NT;
         uint64_t x[Q];
@@ -649,7 +622,7 @@ __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
             c += win ? 1u : 0u;
         }
         __syncthreads();  // every scan buffer is free again
-        uint32_t slot = block_scan<NT>(c, S.wsum[0], cnt);
+        uint32_t slot = block_scan<NT>(c, S.R.wsum[0], cnt);
 #pragma unroll
         for (int q = 0; q < Q; ++q)
             if ((wm >> q) & 1u) {
@@ -681,7 +654,7 @@ __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
             }
         __syncthreads();
         uint32_t tot2;
-        const uint32_t ex2 = block_scan<NT>((uint32_t)__popc(wr[0]) | ((uint32_t)__popc(wr[1]) << 16), S.wsum[0],
+        const uint32_t ex2 = block_scan<NT>((uint32_t)__popc(wr[0]) | ((uint32_t)__popc(wr[1]) << 16), S.R.wsum[0],
                                             tot2);
         uint32_t o[kRuns] = {ex2 & 0xffffu, (tot2 & 0xffffu) + (ex2 >> 16)};
         cnt = (tot2 & 0xffffu) + (tot2 >> 16);
@@ -698,17 +671,36 @@ __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
 }
 
 // ---------------------------------------------------------------- longer rows
+// Three launches over chunks of 4096 values (256 threads), ordered by kernel boundaries:
+//   bound   - per chunk, for two ranks (R1 for every wavefront of the row contributing, R2 = 2 R1
+//             for half of them, as in rows that are mostly -inf): the smallest contribution of
+//             its wavefronts and their number, written to the chunk's slot of the workspace (no
+//             atomics);
+//   collect - every block reduces its row's chunk slots to T0 and appends its values at or above
+//             T0 to the row's candidate list (one reservation atomic per block);
+//   finish  - one block per row stages the candidates in LDS (when they fit), runs the radix
+//             passes, orders the winners by position (LDS bitmap for pool block ids, else a
+//             bitonic sort), writes them and clears the row's candidate count.
+constexpr int kLargeThreads = 256;
+constexpr int kChunk = kLargeThreads * kRunSlots;
+constexpr int kFinishThreads = 1024;
+constexpr int kFinishCap = 8192;  // candidates staged in LDS by the finishing block
+
+struct ChunkBound {
+    uint32_t t0[2];     // smallest contribution for R1, R2 (0xffffffff when none)
+    uint32_t waves[2];  // contributing wavefronts
+};
+
 struct RowState {
-    uint32_t n_sure;
     uint32_t n_cand;
+    uint32_t t0;
     uint32_t pad[30];  // one 128-byte line per row
 };
 
 struct WsView {
-    RowState* st;     // [nq]
-    uint32_t* hist;   // [nq][2048]
-    uint64_t* sure;   // [nq][2048]
-    uint64_t* cand;   // [nq][cap]
+    RowState* st;       // [nq]
+    ChunkBound* bound;  // [nq][chunks]
+    uint64_t* cand;     // [nq][cap]
     int64_t cap;
     int64_t chunks;
 };
@@ -720,133 +712,167 @@ __host__ __device__ inline WsView ws_view(void* ws, int32_t nq, int64_t cap) {
     char* p = (char*)ws;
     v.st = (RowState*)p;
     p += align_up((size_t)nq * sizeof(RowState));
-    v.hist = (uint32_t*)p;
-    p += align_up((size_t)nq * kHistBins * 4);
-    v.sure = (uint64_t*)p;
-    p += align_up((size_t)nq * kMaxK * 8);
+    v.bound = (ChunkBound*)p;
+    p += align_up((size_t)nq * (size_t)v.chunks * sizeof(ChunkBound));
     v.cand = (uint64_t*)p;
     return v;
 }
 
-__global__ __launch_bounds__(kLargeThreads) void select_hist_kernel(SelectArgs a, WsView v) {
-    __shared__ Hist<kLargeThreads> H;
+__global__ __launch_bounds__(kLargeThreads) void select_bound_kernel(SelectArgs a, WsView ws) {
+    constexpr int NW = kLargeThreads / 64;
+    __shared__ uint32_t wt[2][NW];
     const int64_t t = blockIdx.y;
     const RowInfo ri = row_info(a, t);
     const int64_t c0 = (int64_t)blockIdx.x * kChunk;
     if (c0 >= ri.len) return;  // uniform per block
-    uint64_t c[kPer];
-    load_composites<kPer>(a, t, ri, c0 + threadIdx.x, kLargeThreads, c);
-    hist_clear_own(H);
+    float v[kRuns][8];
+    uint32_t pb[kRuns];
+    chunk_load<kLargeThreads>(a, t, ri, c0, v, pb);
+    const uint32_t lm = lane_max(v);
+    const int64_t chunks = (ri.len + kChunk - 1) / kChunk;
+    const uint32_t t1 = wave_rth(lm, bound_rank((uint32_t)a.k, chunks * NW, 1));
+    const uint32_t t2 = wave_rth(lm, bound_rank((uint32_t)a.k, chunks * NW, 2));
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) {
+        wt[0][w] = t1;
+        wt[1][w] = t2;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        ChunkBound cb{{0xffffffffu, 0xffffffffu}, {0u, 0u}};
 #pragma unroll
-    for (int j = 0; j < kPer; ++j)
-        if (c[j]) hist_add(H, (uint32_t)(c[j] >> 53));
-    __syncthreads();
-    hist_reduce(H);
-    __syncthreads();
-    uint32_t* rh = v.hist + t * kHistBins;
-    for (int b = threadIdx.x; b < kHistBins; b += kLargeThreads)
-        if (H.h[hidx(b)]) atomicAdd(&rh[b], H.h[hidx(b)]);
-}
-
-// append with one LDS atomic per wavefront
-__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
-    const uint64_t m = __ballot(pred);
-    if (m == 0) return 0;
-    const int lane = threadIdx.x & 63;
-    const int leader = __ffsll((unsigned long long)m) - 1;
-    uint32_t base = 0;
-    if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
-    base = __shfl(base, leader);
-    return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-}
-
-__global__ __launch_bounds__(kLargeThreads) void select_filter_kernel(SelectArgs a, WsView v) {
-    __shared__ uint32_t h[kPadBins];
-    __shared__ uint64_t lsure[kMaxK];
-    __shared__ uint64_t lcand[kChunk];
-    __shared__ Sel sel;
-    __shared__ uint32_t ns, nc, bs, bc;
-    const int64_t t = blockIdx.y;
-    const RowInfo ri = row_info(a, t);
-    const int64_t c0 = (int64_t)blockIdx.x * kChunk;
-    if (c0 >= ri.len) return;  // uniform per block
-    uint64_t c[kPer];
-    load_composites<kPer>(a, t, ri, c0 + threadIdx.x, kLargeThreads, c);
-    const uint32_t* rh = v.hist + t * kHistBins;
-    for (int b = threadIdx.x; b < kHistBins; b += kLargeThreads) h[hidx(b)] = rh[b];
-    if (threadIdx.x == 0) {
-        ns = 0;
-        nc = 0;
-    }
-    __syncthreads();
-    block_threshold(h, (uint32_t)a.k, sel);
-    const int d1 = sel.digit;
+        for (int i = 0; i < NW; ++i) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int bin = c[j] ? (int)(c[j] >> 53) : -2;
-        const bool sure = c[j] != 0 && bin > d1;
-        const bool on = c[j] != 0 && bin == d1;
-        const uint32_t ps = wave_append(sure, &ns);
-        const uint32_t pc = wave_append(on, &nc);
-        if (sure && ps < (uint32_t)kMaxK) lsure[ps] = c[j];
-        if (on) lcand[pc] = c[j];
+            for (int j = 0; j < 2; ++j)
+                if (wt[j][i]) {
+                    cb.t0[j] = wt[j][i] < cb.t0[j] ? wt[j][i] : cb.t0[j];
+                    ++cb.waves[j];
+                }
+        }
+        ws.bound[t * ws.chunks + blockIdx.x] = cb;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        bs = ns ? atomicAdd(&v.st[t].n_sure, ns) : 0u;
-        bc = nc ? atomicAdd(&v.st[t].n_cand, nc) : 0u;
-    }
-    __syncthreads();
-    uint64_t* gs = v.sure + t * kMaxK;
-    uint64_t* gc = v.cand + t * v.cap;
-    for (uint32_t i = threadIdx.x; i < ns; i += kLargeThreads)
-        if (bs + i < (uint32_t)kMaxK) gs[bs + i] = lsure[i];
-    for (uint32_t i = threadIdx.x; i < nc; i += kLargeThreads) gc[bc + i] = lcand[i];
 }
 
-__global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(SelectArgs a, WsView v) {
-    __shared__ Hist<kFinishThreads> H;
-    __shared__ uint64_t out[kMaxK];
-    __shared__ uint32_t bits[kBitmapMax / 32];
-    __shared__ uint32_t wsum[64];
-    __shared__ Sel sel;
-    __shared__ uint32_t ns, nall;
-    const int64_t t = blockIdx.x;
-    uint32_t* rh = v.hist + t * kHistBins;
-    for (int b = threadIdx.x; b < kHistBins; b += kFinishThreads) H.h[hidx(b)] = rh[b];
-    const uint32_t nsure = v.st[t].n_sure;
-    const uint32_t ncand = v.st[t].n_cand;
-    const uint64_t* gs = v.sure + t * kMaxK;
-    const uint64_t* gc = v.cand + t * v.cap;
-    for (uint32_t i = threadIdx.x; i < nsure && i < (uint32_t)kMaxK; i += kFinishThreads) out[i] = gs[i];
-    if (threadIdx.x == 0) ns = nsure < (uint32_t)kMaxK ? nsure : (uint32_t)kMaxK;
-    __syncthreads();
-    block_threshold(H.h, (uint32_t)a.k, sel);
-    const int d1 = sel.digit;
-    // leave the row histogram and counters cleared for the next call
-    for (int b = threadIdx.x; b < kHistBins; b += kFinishThreads) rh[b] = 0u;
-    if (threadIdx.x == 0) {
-        v.st[t].n_sure = 0u;
-        v.st[t].n_cand = 0u;
-    }
-    if (d1 >= 0 && nsure < (uint32_t)a.k) {
-        auto each = [&](auto&& f) {
-            for (uint32_t i = threadIdx.x; i < ncand; i += kFinishThreads) f(gc[i]);
-        };
-        uint32_t need = (uint32_t)a.k - nsure;
-        uint64_t prefix = (uint64_t)d1 << 53, mask = ~0ull << 53, T = ~0ull;
-        for (int p = 1; p < 6; ++p)
-            if (radix_pass<kFinishThreads>(each, p, need, prefix, mask, T, H, sel)) break;
-        for (uint32_t i0 = 0; i0 < ncand; i0 += kFinishThreads) {
-            const uint32_t i = i0 + threadIdx.x;
-            const uint64_t c = i < ncand ? gc[i] : 0ull;
-            const bool take = c != 0 && c >= T;
-            const uint32_t slot = wave_append(take, &ns);
-            if (take && slot < (uint32_t)kMaxK) out[slot] = c;
+// T0 of row t from its chunk bounds, by the whole block
+template <int NT>
+__device__ __forceinline__ uint32_t row_bound(const SelectArgs& a, const WsView& ws, int64_t t, int64_t chunks,
+                                              uint32_t* red) {
+    constexpr int NW = NT / 64;
+    uint32_t t0[2] = {0xffffffffu, 0xffffffffu}, nw[2] = {0u, 0u};
+    for (int64_t c = threadIdx.x; c < chunks; c += NT) {
+        const ChunkBound cb = ws.bound[t * ws.chunks + c];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            t0[j] = cb.t0[j] < t0[j] ? cb.t0[j] : t0[j];
+            nw[j] += cb.waves[j];
         }
     }
+    // wavefront reductions (min as the max of complements), then across wavefronts
+    const uint32_t r0 = wave_incl_max(~t0[0]), r1 = wave_incl_max(~t0[1]), r2 = wave_incl_add(nw[0]),
+                   r3 = wave_incl_add(nw[1]);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 63) {
+        red[w] = r0;
+        red[NW + w] = r1;
+        red[2 * NW + w] = r2;
+        red[3 * NW + w] = r3;
+    }
     __syncthreads();
-    const uint32_t cnt = ns < (uint32_t)a.k ? ns : (uint32_t)a.k;
+    uint32_t n0 = 0u, n1 = 0u, c0 = 0u, c1 = 0u;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        n0 = red[i] > n0 ? red[i] : n0;
+        n1 = red[NW + i] > n1 ? red[NW + i] : n1;
+        c0 += red[2 * NW + i];
+        c1 += red[3 * NW + i];
+    }
+    const int64_t waves = chunks * (kLargeThreads / 64);
+    const uint64_t k = (uint64_t)a.k;
+    if ((uint64_t)c0 * bound_rank(a.k, waves, 1) >= k) return ~n0;
+    if ((uint64_t)c1 * bound_rank(a.k, waves, 2) >= k) return ~n1;
+    return 0u;
+}
+
+__global__ __launch_bounds__(kLargeThreads) void select_collect_kernel(SelectArgs a, WsView ws) {
+    constexpr int NW = kLargeThreads / 64;
+    __shared__ uint32_t red[4 * NW];
+    __shared__ uint32_t wsum[NW];
+    __shared__ uint32_t base;
+    const int64_t t = blockIdx.y;
+    const RowInfo ri = row_info(a, t);
+    const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+    if (c0 >= ri.len) return;  // uniform per block
+    float v[kRuns][8];
+    uint32_t pb[kRuns];
+    chunk_load<kLargeThreads>(a, t, ri, c0, v, pb);
+    const int64_t chunks = (ri.len + kChunk - 1) / kChunk;
+    const uint32_t T0 = row_bound<kLargeThreads>(a, ws, t, chunks, red);
+    if (blockIdx.x == 0 && threadIdx.x == 0) ws.st[t].t0 = T0;
+    const float fT = T0 ? key_value(T0) : -__FLT_MAX__;
+    uint32_t c = 0;
+#pragma unroll
+    for (int r = 0; r < kRuns; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c += v[r][e] >= fT ? 1u : 0u;
+    uint32_t tot;
+    uint32_t o = block_scan<kLargeThreads>(c, wsum, tot);
+    if (threadIdx.x == 0) base = tot ? atomicAdd(&ws.st[t].n_cand, tot) : 0u;
+    __syncthreads();
+    uint64_t* out = ws.cand + t * ws.cap + base;
+#pragma unroll
+    for (int r = 0; r < kRuns; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (v[r][e] >= fT) out[o++] = list_entry(v[r][e], pb[r] + (uint32_t)e);
+}
+
+__global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(SelectArgs a, WsView ws) {
+    __shared__ uint64_t list[kFinishCap];
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ RadixShared<kFinishThreads> S;
+    __shared__ uint64_t out[kMaxK];
+    __shared__ uint32_t bits[kBitmapMax / 32];
+    const int64_t t = blockIdx.x;
+    const uint32_t C = ws.st[t].n_cand, T0 = ws.st[t].t0;
+    const uint32_t k = (uint32_t)a.k;
+    const uint64_t* gc = ws.cand + t * ws.cap;
+    const uint64_t* L = gc;
+    if (C <= (uint32_t)kFinishCap) {
+        for (uint32_t i = threadIdx.x; i < C; i += kFinishThreads) list[i] = gc[i];
+        L = list;
+    }
+    __syncthreads();
+    const uint64_t T = C > k ? list_radix<kFinishThreads>(L, C, k, T0, hist, S) : 1ull;
+    // the winners, gathered in rounds of 8 consecutive entries per thread
+    constexpr int Q = 8;
+    uint32_t nw = 0;
+    int sb = 0;
+    for (uint32_t i0 = 0; i0 < C; i0 += Q * kFinishThreads) {
+        uint64_t x[Q];
+        uint32_t wm = 0, c = 0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const uint32_t i = i0 + Q * threadIdx.x + q;
+            x[q] = i < C ? entry_composite(L[i]) : 0ull;
+            const bool win = i < C && x[q] >= T;
+            wm |= (win ? 1u : 0u) << q;
+            c += win ? 1u : 0u;
+        }
+        __syncthreads();  // the scan buffer of two rounds ago is free
+        uint32_t tot;
+        uint32_t slot = nw + block_scan<kFinishThreads>(c, S.wsum[sb], tot);
+        sb ^= 1;
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+            if ((wm >> q) & 1u) {
+                if (slot < (uint32_t)kMaxK) out[slot] = x[q];
+                ++slot;
+            }
+        nw += tot;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) ws.st[t].n_cand = 0u;  // cleared for the next call
+    const uint32_t cnt = nw < k ? nw : k;
     const RowInfo ri = row_info(a, t);
     if (a.pool_mode && ri.len <= kBitmapMax) {
         // ascending block ids through an LDS bitmap and a block-wide prefix sum
@@ -863,7 +889,8 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(SelectArg
         uint32_t mine = 0;
         for (int q = 0; q < per; ++q)
             if (w0 + q < words) mine += (uint32_t)__popc(bits[w0 + q]);
-        uint32_t base = block_exclusive_scan<kFinishThreads>(mine, wsum, &nall);
+        uint32_t nall;
+        uint32_t base = block_scan<kFinishThreads>(mine, S.wsum[0], nall);
         for (int q = 0; q < per; ++q) {
             if (w0 + q >= words) break;
             uint32_t b = bits[w0 + q];
@@ -898,8 +925,8 @@ size_t select_workspace_bytes(int32_t nq, int64_t cap, int32_t k) {
     if (nq <= 0 || cap < 0) return 0;
     if (cap <= kSmallRow) return 256;
     const WsView v = ws_view(nullptr, nq, cap);
-    return align_up((size_t)nq * sizeof(RowState)) + align_up((size_t)nq * kHistBins * 4) +
-           align_up((size_t)nq * kMaxK * 8) + align_up((size_t)nq * (size_t)v.cap * 8);
+    return align_up((size_t)nq * sizeof(RowState)) + align_up((size_t)nq * (size_t)v.chunks * sizeof(ChunkBound)) +
+           align_up((size_t)nq * (size_t)v.cap * 8);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
@@ -919,9 +946,9 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
         return hipGetLastError();
     }
     const WsView v = ws_view(a.ws, a.nq, cap);
-    hipLaunchKernelGGL(select_hist_kernel, dim3((unsigned)v.chunks, (unsigned)a.nq), dim3(kLargeThreads), 0, stream,
+    hipLaunchKernelGGL(select_bound_kernel, dim3((unsigned)v.chunks, (unsigned)a.nq), dim3(kLargeThreads), 0, stream,
                        a, v);
-    hipLaunchKernelGGL(select_filter_kernel, dim3((unsigned)v.chunks, (unsigned)a.nq), dim3(kLargeThreads), 0,
+    hipLaunchKernelGGL(select_collect_kernel, dim3((unsigned)v.chunks, (unsigned)a.nq), dim3(kLargeThreads), 0,
                        stream, a, v);
     hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)a.nq), dim3(kFinishThreads), 0, stream, a, v);
     return hipGetLastError();
