@@ -194,8 +194,9 @@ idx_status idx_score_pool_gather(const uint8_t* k_codes, const uint8_t* k_scales
  *                  reported index and the tie-break key.
  *   block        : 8 when blocks is given (ignored otherwise).
  *   out_idx      : device int32 [nq][out_stride], out_stride >= k.
- *   out_val      : device fp32 [nq][out_stride] or NULL: the selected values in the same order,
- *                  -inf after them.
+ *   out_val      : device fp32 [nq][out_stride] or NULL: the selected values in the same order
+ *                  (-0 and +0 are equal values and a selected zero is reported as +0), -inf
+ *                  after them.
  *   ws, ws_bytes : at least idx_workspace_size(IDX_OP_TOPK, nq, max_n, k) bytes, 16-byte aligned,
  *                  zero-filled before first use; every call restores its counters (as for
  *                  idx_build_pool); separate workspaces for calls that may run concurrently.

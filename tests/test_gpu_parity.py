@@ -5,6 +5,8 @@ them exactly representable, which the synthetic recipe always satisfies); scores
 A = sum_j |w_j| ReLU(d_j); selections identical except entries within that tolerance of the k-th
 value; selections over identical fp32 inputs identical.
 """
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -145,6 +147,65 @@ def test_topk_exact(fx, n, k, kind):
         assert (out[t, cnt:] == -1).all()
         assert np.array_equal(oval[t, :cnt], vals[t, ref_pos])
         assert np.all(np.isneginf(oval[t, cnt:]))
+
+
+def adversarial_rows(rng, nq, n, kind, k):
+    """rows aimed at the candidate bound and the list passes of the selection"""
+    if kind == "posinf_few":  # fewer +inf than k: counted before the passes
+        a = rng.standard_normal((nq, n)).astype(np.float32)
+        a[:, rng.choice(n, size=min(n, max(1, k // 3)), replace=False)] = np.inf
+        return a
+    if kind == "posinf_many":  # more +inf than k: positions decide among them
+        a = rng.standard_normal((nq, n)).astype(np.float32)
+        a[:, rng.choice(n, size=min(n, 2 * k + 3), replace=False)] = np.inf
+        return a
+    if kind == "nan":
+        a = rng.standard_normal((nq, n)).astype(np.float32)
+        a[rng.random((nq, n)) < 0.2] = np.nan
+        return a
+    if kind == "signed_zeros":  # -0 and +0 tie; a few positives and negatives around them
+        a = np.where(rng.random((nq, n)) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+        m = rng.random((nq, n))
+        a[m < k / (4 * n)] = 1.0
+        a[(m > 0.5) & (m < 0.6)] = -1.0
+        return a
+    if kind == "narrow":  # keys that differ only in the low mantissa bits
+        return (np.float32(3.0) + rng.integers(0, 300, (nq, n)).astype(np.float32) * np.float32(2.0 ** -20))
+    if kind == "sparse":  # mostly -inf: few eligible values, spread over the row
+        a = np.full((nq, n), -np.inf, np.float32)
+        idx = rng.choice(n, size=min(n, 3 * k), replace=False)
+        a[:, idx] = rng.standard_normal(len(idx)).astype(np.float32)
+        return a
+    if kind == "one_hot":  # a single huge value among ties
+        a = np.zeros((nq, n), np.float32)
+        a[:, n // 3] = 1e30
+        return a
+    raise KeyError(kind)
+
+
+@pytest.mark.parametrize("kind", ["posinf_few", "posinf_many", "nan", "signed_zeros", "narrow", "sparse", "one_hot"])
+@pytest.mark.parametrize("n,k", [(16384, 512), (5000, 1025), (3000, 1), (70000, 512), (200000, 2048), (40000, 64)])
+def test_topk_adversarial(fx, n, k, kind):
+    rng = np.random.default_rng(zlib.crc32(f"{n},{k},{kind}".encode()))
+    nq = 2
+    vals = adversarial_rows(rng, nq, n, kind, k)
+    nvalid = np.array([n, max(1, n - 37)], dtype=np.int32)
+    ws = fx.workspace(fx.IDX_OP_TOPK, nq, n, k)
+    out = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
+    oval = torch.empty((nq, k), dtype=torch.float32, device="cuda")
+    for _ in range(2):  # the second call reuses the workspace as the first left it
+        fx.idx_topk(torch.from_numpy(vals).cuda(), n, k, out, ws, n_valid=torch.from_numpy(nvalid).cuda(),
+                    out_val=oval)
+        torch.cuda.synchronize()
+        o, ov = out.cpu().numpy(), oval.cpu().numpy()
+        for t in range(nq):
+            ref = oracle.topk(vals[t, :nvalid[t]].astype(np.float64), k)
+            cnt = int((ref >= 0).sum())
+            ref_pos = np.sort(ref[:cnt])
+            assert np.array_equal(o[t, :cnt], ref_pos), f"row {t}"
+            assert (o[t, cnt:] == -1).all()
+            assert np.array_equal(ov[t, :cnt], vals[t, ref_pos])  # -0 == +0
+            assert np.all(np.isneginf(ov[t, cnt:]))
 
 
 @pytest.mark.parametrize("n,k", [(4096, 512), (8000, 512), (16384, 512)])

@@ -27,8 +27,11 @@ constexpr int64_t kBitmapMax = (int64_t)1 << 18;  // pool rows up to this many b
 
 __device__ __forceinline__ int hidx(int b) { return b + (b >> 5); }
 
+// order-preserving key of a float; -0 and +0 share the key of +0 (equal values tie, and ties go
+// to the lower index)
 __device__ __forceinline__ uint32_t order_key(float f) {
-    const uint32_t u = __float_as_uint(f);
+    uint32_t u = __float_as_uint(f);
+    u = u == 0x80000000u ? 0u : u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 __device__ __forceinline__ float key_value(uint32_t k) {
@@ -372,8 +375,7 @@ __device__ __forceinline__ void chunk_load(const SelectArgs& a, int64_t t, const
     }
 }
 
-// key of the thread's largest value, a zero maximum counted as -0 (a lower bound); 0 when the
-// thread holds no eligible value
+// key of the thread's largest value; 0 when the thread holds no eligible value
 __device__ __forceinline__ uint32_t lane_max(const float (&v)[kRuns][8]) {
     float fm = v[0][0];
 #pragma unroll
@@ -583,7 +585,7 @@ __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
     if (lane == 0) atomicMin(&S.t0, t0w);
     __syncthreads();
     const uint32_t T0 = S.t0;
-    const float fT = T0 ? key_value(T0) : -__FLT_MAX__;  // v >= fT: every value with key >= T0 (and -0 at +0)
+    const float fT = T0 ? key_value(T0) : -__FLT_MAX__;  // v >= fT: exactly the values with key >= T0
 
     // 2. candidates: counts per run, packed, one scan gives slot-order offsets
     uint32_t cr[kRuns];
