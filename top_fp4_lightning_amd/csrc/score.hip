@@ -219,7 +219,15 @@ __global__ __launch_bounds__(256) void score_gather_kernel(GatherArgs a) {
 }
 
 constexpr int kScanIters = 4;    // 4 waves x 4 steps x 64 keys = 1024 keys per block
+// Pool gather: one 64-slot step per wavefront when the launch is small (a decode step: the latency
+// of a few short-lived waves), several steps when it is large (prefill: the query is loaded once
+// per wavefront and the next step's keys are in flight while the current step computes).
 constexpr int kGatherIters = 1;
+#ifndef FP4IDX_GATHER_ITERS_MANY
+#define FP4IDX_GATHER_ITERS_MANY 4
+#endif
+constexpr int kGatherItersMany = FP4IDX_GATHER_ITERS_MANY;
+constexpr int64_t kGatherManySlots = (int64_t)1 << 22;  // slots per launch from which the long form runs
 }  // namespace
 
 hipError_t launch_score_full(const ScoreArgs& a, hipStream_t stream) {
@@ -233,11 +241,18 @@ hipError_t launch_score_full(const ScoreArgs& a, hipStream_t stream) {
 
 hipError_t launch_score_gather(const GatherArgs& a, hipStream_t stream) {
     if (a.nq <= 0 || a.max_blocks <= 0) return hipSuccess;
-    const int64_t per_block = 4 * kGatherIters * 64;
     const int64_t slots = (int64_t)a.max_blocks * kBlock;
-    const int64_t gx = (slots + per_block - 1) / per_block;
-    hipLaunchKernelGGL(score_gather_kernel<kGatherIters>, dim3((unsigned)gx, (unsigned)a.nq), dim3(256), 0, stream,
-                       a);
+    if ((int64_t)a.nq * slots >= kGatherManySlots) {
+        const int64_t per_block = 4 * kGatherItersMany * 64;
+        const int64_t gx = (slots + per_block - 1) / per_block;
+        hipLaunchKernelGGL(score_gather_kernel<kGatherItersMany>, dim3((unsigned)gx, (unsigned)a.nq), dim3(256), 0,
+                           stream, a);
+    } else {
+        const int64_t per_block = 4 * kGatherIters * 64;
+        const int64_t gx = (slots + per_block - 1) / per_block;
+        hipLaunchKernelGGL(score_gather_kernel<kGatherIters>, dim3((unsigned)gx, (unsigned)a.nq), dim3(256), 0,
+                           stream, a);
+    }
     return hipGetLastError();
 }
 
