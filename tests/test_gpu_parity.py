@@ -357,14 +357,16 @@ def test_topk_with_block_map(fx, nblocks, k):
 
 
 @pytest.mark.parametrize("outputs", ["both", "block_max", "scores"])
-@pytest.mark.parametrize("n_keys,nqs,group", [(6000, 48, 48), (3000, 37, 37), (20000, 70, 35), (9000, 16, 16)])
+@pytest.mark.parametrize("n_keys,nqs,group", [(6000, 48, 48), (3000, 37, 37), (20000, 70, 35), (9000, 16, 16),
+                                              # groups that run three-wave blocks
+                                              (7000, 30, 6), (5000, 10, 5), (3000, 9, 3), (12000, 36, 6)])
 def test_multi_query_scan_matches_single_query(fx, pl, n_keys, nqs, group, outputs):
     # the many-query scan (group > 1) must reproduce the per-query scan bit for bit, for each
     # combination of requested outputs (untouched entries stay NaN on both sides)
     wl = synth.prefill_workload("mq", 205 + nqs, n_keys, nqs)
     dev = pl.DeviceWorkload.from_workload(wl, group=group)
-    if group < nqs:  # two groups over the same keys, the second with its own causal bounds
-        dev.n_vis = torch.cat([dev.n_vis[:group], dev.n_vis[:group] - 1000])
+    if group < nqs:  # several groups over the same keys, each with its own causal bounds
+        dev.n_vis = torch.cat([dev.n_vis[:group] - 1000 * i for i in range(nqs // group)])
     qc, qs = fx.idx_quantize_q(dev.q[0], dev.signs)
     nb = (dev.max_n + 7) // 8
     want_sc = outputs in ("both", "scores")
