@@ -127,7 +127,10 @@ def make_rows(rng, nq, n, kind):
                                       # block-size boundaries of the short-row kernel (256 / 512 / 1024
                                       # threads), and candidate lists beyond the smaller LDS list
                                       (4096, 512, "normal"), (4097, 512, "normal"), (8192, 2048, "normal"),
-                                      (8193, 512, "ties"), (4096, 2048, "equal"), (4000, 512, "ties")])
+                                      (8193, 512, "ties"), (4096, 2048, "equal"), (4000, 512, "ties"),
+                                      # long rows whose bound admits every value (k large for the row),
+                                      # so the candidates exceed what the finishing block stages in LDS
+                                      (20000, 2048, "normal"), (33000, 2048, "neginf"), (16385, 1, "ties")])
 def test_topk_exact(fx, n, k, kind):
     rng = np.random.default_rng(n + k)
     nq = 3
