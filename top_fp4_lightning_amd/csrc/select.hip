@@ -416,10 +416,11 @@ struct RadixShared {
 
 constexpr uint32_t kInfKey = 0xff800000u;  // order key of +inf
 
-// T for the candidates L[0 .. C) (C > k, at least k of them with keys >= T0); hist is a 2048-bin
-// scratch histogram. Called by the whole block; contains barriers. +inf entries (the pinned
-// block, +inf values) are counted first and kept out of the passes, so that the first digit
-// starts below the bits shared by T0 and the largest finite key.
+// T for the candidates L[0 .. C) (C > k, at least k of them with keys >= T0); hist holds two
+// 2048-bin scratch histograms (passes alternate between them, so that clearing the next one
+// needs no barrier of its own). Called by the whole block; contains barriers. +inf entries (the
+// pinned block, +inf values) are counted first and kept out of the passes, so that the first
+// digit starts below the bits shared by T0 and the largest finite key.
 template <int NT>
 __device__ uint64_t list_radix(const uint64_t* L, uint32_t C, uint32_t k, uint32_t T0, uint32_t* hist,
                                RadixShared<NT>& S) {
@@ -430,7 +431,10 @@ __device__ uint64_t list_radix(const uint64_t* L, uint32_t C, uint32_t k, uint32
         S.digit = 0;
         S.above = 0u;
         S.T = 1ull;
+        S.nfin = 0u;
     }
+    if (tid < 64) S.rk[tid] = 0u;
+    for (int b = tid; b < kHistBins; b += NT) hist[b] = 0u;  // the first pass's histogram
     uint32_t km = 0u, ni = 0u;
     for (uint32_t i = tid; i < C; i += NT) {
         const uint32_t kk = order_key(__uint_as_float((uint32_t)(L[i] >> 32)));
@@ -470,23 +474,24 @@ __device__ uint64_t list_radix(const uint64_t* L, uint32_t C, uint32_t k, uint32
         lim = (uint64_t)kInfKey << 32;
     }
     int sb = 0;
-    for (;;) {
+    for (int pass = 0;; ++pass) {
         const int width = hi + 1 < 11 ? hi + 1 : 11;
         const int lo = hi - width + 1;
         const uint64_t dm = (1ull << width) - 1ull;
-        __syncthreads();  // readers of the previous histogram are done
-        for (int b = tid; b < kHistBins; b += NT) hist[b] = 0u;
-        __syncthreads();
+        uint32_t* h = hist + (pass & 1) * kHistBins;
         for (uint32_t i = tid; i < C; i += NT) {
             const uint64_t x = entry_composite(L[i]);
-            if (((x ^ prefix) & mask) == 0 && x < lim) atomicAdd(&hist[(x >> lo) & dm], 1u);
+            if (((x ^ prefix) & mask) == 0 && x < lim) atomicAdd(&h[(x >> lo) & dm], 1u);
         }
         __syncthreads();
+        // every thread is past the previous pass's reads of the other histogram: clear it for
+        // the next pass (two more barriers separate this from the next pass's adds)
+        for (int b = tid; b < kHistBins; b += NT) hist[((pass + 1) & 1) * kHistBins + b] = 0u;
         {  // threshold digit: thread tid owns bins kHistBins - 1 - (B * tid + j), j < B
             uint32_t c[B], sum = 0;
 #pragma unroll
             for (int j = 0; j < B; ++j) {
-                c[j] = hist[kHistBins - 1 - (B * tid + j)];
+                c[j] = h[kHistBins - 1 - (B * tid + j)];
                 sum += c[j];
             }
             uint32_t tot;
@@ -508,7 +513,7 @@ __device__ uint64_t list_radix(const uint64_t* L, uint32_t C, uint32_t k, uint32
         }
         const int d = S.digit;
         const uint32_t above = S.above;
-        const uint32_t on = hist[d];
+        const uint32_t on = h[d];
         if (on == need - above) return prefix | ((uint64_t)d << lo);
         need -= above;
         prefix |= (uint64_t)d << lo;
@@ -516,10 +521,7 @@ __device__ uint64_t list_radix(const uint64_t* L, uint32_t C, uint32_t k, uint32
         hi = lo - 1;
         if (on <= 64 || hi < 0) break;
     }
-    // the few elements on the digit, ranked against each other
-    if (tid == 0) S.nfin = 0u;
-    if (tid < 64) S.rk[tid] = 0u;
-    __syncthreads();
+    // the few elements on the digit, ranked against each other (counters cleared at the start)
     for (uint32_t i = tid; i < C; i += NT) {
         const uint64_t x = entry_composite(L[i]);
         if (((x ^ prefix) & mask) == 0 && x < lim) {
@@ -557,11 +559,12 @@ struct SmallShared {
         Hist<NT> H;  // register passes
         struct {
             uint64_t list[kCap];
-            uint32_t hist[kHistBins];
+            uint32_t hist[2 * kHistBins];
         } L;
     };
     RadixShared<NT> R;
-    uint32_t t0;
+    uint32_t wt0[NT / 64];   // each wavefront's contribution to T0
+    uint32_t wout[NT / 64];  // scan buffer of the output step
     Sel sel;
 };
 
@@ -572,8 +575,7 @@ __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
     __shared__ SmallShared<NT> S;
     const int64_t t = blockIdx.x;
     const RowInfo ri = row_info(a, t);
-    const int tid = threadIdx.x, lane = tid & 63;
-    if (tid == 0) S.t0 = 0xffffffffu;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     float v[kRuns][8];
     uint32_t pb[kRuns];
     chunk_load<NT>(a, t, ri, 0, v, pb);
@@ -581,10 +583,11 @@ __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
     // 1. T0 (every wavefront must contribute here)
     const uint32_t R = ((uint32_t)a.k + NW - 1) / NW;
     const uint32_t t0w = R <= 64 ? wave_rth(lane_max(v), R) : 0u;
+    if (lane == 0) S.wt0[w] = t0w;
     __syncthreads();
-    if (lane == 0) atomicMin(&S.t0, t0w);
-    __syncthreads();
-    const uint32_t T0 = S.t0;
+    uint32_t T0 = S.wt0[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) T0 = S.wt0[i] < T0 ? S.wt0[i] : T0;
     const float fT = T0 ? key_value(T0) : -__FLT_MAX__;  // v >= fT: exactly the values with key >= T0
 
     // 2. candidates: counts per run, packed, one scan gives slot-order offsets
@@ -623,8 +626,7 @@ __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
             wm |= (win ? 1u : 0u) << q;
             c += win ? 1u : 0u;
         }
-        __syncthreads();  // every scan buffer is free again
-        uint32_t slot = block_scan<NT>(c, S.R.wsum[0], cnt);
+        uint32_t slot = block_scan<NT>(c, S.wout, cnt);
 #pragma unroll
         for (int q = 0; q < Q; ++q)
             if ((wm >> q) & 1u) {
@@ -830,7 +832,7 @@ __global__ __launch_bounds__(kLargeThreads) void select_collect_kernel(SelectArg
 
 __global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(SelectArgs a, WsView ws) {
     __shared__ uint64_t list[kFinishCap];
-    __shared__ uint32_t hist[kHistBins];
+    __shared__ uint32_t hist[2 * kHistBins];
     __shared__ RadixShared<kFinishThreads> S;
     __shared__ uint64_t out[kMaxK];
     __shared__ uint32_t bits[kBitmapMax / 32];
