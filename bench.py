@@ -166,7 +166,7 @@ def bench_decode(wl, args) -> int:
     plan = pipeline.DecodePlan(dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(ev=None, gev=None):
         plan.quantize(0)
         if ev is not None:
             ev[0].record(stream)
@@ -174,7 +174,7 @@ def bench_decode(wl, args) -> int:
         if ev is not None:
             ev[1].record(stream)
         plan.build_pool()
-        plan.pool_select(0)
+        plan.pool_select(0, events=gev)
         for layer in range(1, plan.layers + 1):
             plan.quantize(layer)
             plan.pool_select(layer)
@@ -182,7 +182,10 @@ def bench_decode(wl, args) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    def pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    evs = [pair() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -191,6 +194,23 @@ def bench_decode(wl, args) -> int:
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1000.0 / args.steps
     scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    # The pool gather, timed outside the timed steps. Cold: the Full layer's gather right after
+    # the scan, whose stream has replaced the cache contents, so its pooled blocks come from HBM
+    # (one event pair per launch, which adds the events' own few microseconds). Warm: the same
+    # gather launched back to back between one event pair, its blocks in the last-level cache, as
+    # for Reindex layers that follow one another with nothing in between.
+    gevs = [pair() for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(None, gevs[i])
+    burst = pair()
+    burst[0].record(stream)
+    for _ in range(args.steps):
+        plan.pool_gather(0)
+    burst[1].record(stream)
+    torch.cuda.synchronize()
+    gather_cold_ms = float(np.mean([a.elapsed_time(b) for a, b in gevs]))
+    gather_warm_ms = burst[0].elapsed_time(burst[1]) / args.steps
     ms_eager = ms_step
     if args.graph:
         # the whole step captured once in a HIP graph (the plan allocates nothing and the library
@@ -235,6 +255,12 @@ def bench_decode(wl, args) -> int:
                     "algorithmic_flop_per_launch": flop, "algorithmic_bytes_per_launch": sb,
                     "hbm_achieved_gbs": sb / (scan_ms / 1000.0) / 1e9,
                     "hbm_frac": sb / (scan_ms / 1000.0) / 1e9 / HBM_PEAK_GBS}
+    # gather: 68 B per pooled key, q (32 x 68 B) + w (128 B) per query, 4 B per score slot written
+    slots = wl.nq * plan.max_blocks * 8
+    gb = pool_pos * 68 + wl.nq * (32 * 68 + 32 * 4) + slots * 4
+    gather = {"kernel": "score_gather_kernel", "algorithmic_bytes_per_launch": gb,
+              "ms_cold": gather_cold_ms, "hbm_frac_cold": gb / (gather_cold_ms / 1000.0) / 1e9 / HBM_PEAK_GBS,
+              "ms_warm": gather_warm_ms, "frac_warm": gb / (gather_warm_ms / 1000.0) / 1e9 / HBM_PEAK_GBS}
     res = {
         "metric": "indexer entries scored/s + top-512 queries/s at 1M ctx; % of HBM roofline",
         "value": entries / (ms_step / 1000.0),
@@ -257,6 +283,7 @@ def bench_decode(wl, args) -> int:
         "step_launch": "hip graph replay" if args.graph else "eager launches",
         "ms_per_step_eager": ms_eager,
         "roofline": roofline,
+        "gather": gather,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)

@@ -174,24 +174,38 @@ __global__ __launch_bounds__(256) void score_gather_kernel(GatherArgs a) {
     const int g = lane >> 4, r = lane & 15;
     const int32_t* blk = a.blocks + t * a.blocks_stride;
 
-    // key index of slot s within the query's range, kAbsent if the slot is empty
-    auto pos_of = [&](int64_t s) -> uint32_t {
-        const int64_t i = s >> 3;
-        if (s >= slots || i >= cnt) return kAbsent;
-        const int64_t b = blk[i];
-        const int64_t pos = b * kBlock + (s & 7);
-        return (b >= 0 && pos < n) ? (uint32_t)pos : kAbsent;
+    // Key indices of one 64-slot step: the four tiles' slots of this lane and the lane's own
+    // output slot. The block ids are read first, all five unconditionally (clamped to the row), so
+    // that the key loads of the four tiles are issued back to back instead of each waiting on its
+    // own id; absent slots (past the count or the row, negative ids, positions >= n) map to kAbsent.
+    auto step_positions = [&](int64_t s0, uint32_t (&pos)[5]) {
+        int32_t b[5];
+#pragma unroll
+        for (int u = 0; u < 5; ++u) {
+            const int64_t s = s0 + (u < 4 ? 16 * u + r : lane);
+            const int64_t i = s >> 3;
+            b[u] = blk[i < a.max_blocks ? i : a.max_blocks - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < 5; ++u) {
+            const int64_t s = s0 + (u < 4 ? 16 * u + r : lane);
+            const int64_t e = (int64_t)b[u] * kBlock + (s & 7);
+            pos[u] = (s < slots && (s >> 3) < cnt && b[u] >= 0 && e < n) ? (uint32_t)e : kAbsent;
+        }
     };
 
+    uint32_t pc[5], pn[5] = {kAbsent, kAbsent, kAbsent, kAbsent, kAbsent};
     KTile cur[4], nxt[4];
+    step_positions(s_begin, pc);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) load_key<kReuse>(kr, pos_of(s_begin + 16 * u + r), g, cur[u]);
+    for (int u = 0; u < 4; ++u) load_key<kReuse>(kr, pc[u], g, cur[u]);
     for (int it = 0; it < ITERS; ++it) {
         const int64_t s0 = s_begin + (int64_t)it * 64;
         if (s0 >= slots) break;
         if (it + 1 < ITERS) {
+            step_positions(s0 + 64, pn);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) load_key<kReuse>(kr, pos_of(s0 + 64 + 16 * u + r), g, nxt[u]);
+            for (int u = 0; u < 4; ++u) load_key<kReuse>(kr, pn[u], g, nxt[u]);
         }
         float p[4];
 #pragma unroll
@@ -199,22 +213,22 @@ __global__ __launch_bounds__(256) void score_gather_kernel(GatherArgs a) {
             TileOut o;
             mfma_tile(q, cur[u], o);
             p[u] = lane_partial(q, o);
-            if (a.head_dots) {
+            if (a.head_dots && pc[u] != kAbsent) {
                 const int64_t s = s0 + 16 * u + r;
-                if (pos_of(s) != kAbsent) {
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
+                for (int h = 0; h < 2; ++h)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            a.head_dots[(t * kHeads + 16 * h + 4 * g + i) * a.score_stride + s] = o.d[h][i];
-                }
+                    for (int i = 0; i < 4; ++i)
+                        a.head_dots[(t * kHeads + 16 * h + 4 * g + i) * a.score_stride + s] = o.d[h][i];
             }
         }
         const float sc = combine4(p[0], p[1], p[2], p[3]);
         const int64_t s = s0 + lane;
-        if (s < slots) a.scores[t * a.score_stride + s] = pos_of(s) != kAbsent ? sc : -INFINITY;
+        if (s < slots) a.scores[t * a.score_stride + s] = pc[4] != kAbsent ? sc : -INFINITY;
 #pragma unroll
         for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+#pragma unroll
+        for (int u = 0; u < 5; ++u) pc[u] = pn[u];
     }
 }
 
@@ -227,7 +241,10 @@ constexpr int kGatherIters = 1;
 #define FP4IDX_GATHER_ITERS_MANY 4
 #endif
 constexpr int kGatherItersMany = FP4IDX_GATHER_ITERS_MANY;
-constexpr int64_t kGatherManySlots = (int64_t)1 << 22;  // slots per launch from which the long form runs
+#ifndef FP4IDX_GATHER_MANY_SLOTS
+#define FP4IDX_GATHER_MANY_SLOTS (1 << 22)
+#endif
+constexpr int64_t kGatherManySlots = FP4IDX_GATHER_MANY_SLOTS;  // slots per launch from which the long form runs
 }  // namespace
 
 hipError_t launch_score_full(const ScoreArgs& a, hipStream_t stream) {

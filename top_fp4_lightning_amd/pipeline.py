@@ -121,11 +121,18 @@ class DecodePlan:
         idx_build_pool(self.block_max, self.dev.n_vis, self.dev.max_n, self.pool_blocks, self.pool_count,
                        self.ws_pool, topk_blocks=self.topk_blocks, stream=stream)
 
-    def pool_select(self, layer: int, stream=None):
+    def pool_gather(self, layer: int, stream=None):
         dv = self.dev
         idx_score_pool_gather(dv.k_codes, dv.k_scales, dv.k_base, dv.n_vis, self.pool_blocks, self.pool_count,
                               self.max_blocks, self.q_codes[layer], self.q_scales[layer], dv.w[layer],
                               self.pool_scores[layer], stream=stream)
+
+    def pool_select(self, layer: int, stream=None, events=None):
+        if events is not None:
+            events[0].record(stream)
+        self.pool_gather(layer, stream)
+        if events is not None:
+            events[1].record(stream)
         idx_topk(self.pool_scores[layer], self.max_blocks * BLOCK, self.k, self.topk[layer], self.ws_topk,
                  out_val=self.topk_val[layer], blocks=self.pool_blocks, stream=stream)
 
