@@ -101,17 +101,25 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(const uint8_t* __restric
                                                         int32_t k, uint16_t* __restrict__ out) {
     const int lane = threadIdx.x & 63;
     const int64_t t = blockIdx.y;
-    const int i0 = ((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * EPW;
-    if (i0 >= k) return;  // uniform per wave
+    // the wave's first entry, uniform across the wave
+    const int i0 = __builtin_amdgcn_readfirstlane(((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * EPW);
+    if (i0 >= k) return;
     const int64_t base = kv_base[t];
     const int64_t n = n_vis[t];
     const int32_t* sel = idx + t * idx_stride;
+    // all EPW positions first (clamped to the row), so that no row load waits on the next position
+    int64_t pos[EPW];
+#pragma unroll
+    for (int j = 0; j < EPW; ++j) {
+        const int i = i0 + j;
+        pos[j] = sel[i < k ? i : k - 1];
+        if (i >= k) pos[j] = -1;
+    }
     uint32_t cw[EPW], sb[EPW];
     bool ok[EPW];
 #pragma unroll
     for (int j = 0; j < EPW; ++j) {
-        const int i = i0 + j;
-        const int64_t p = i < k ? (int64_t)sel[i] : -1;
+        const int64_t p = pos[j];
         ok[j] = p >= 0 && p < n;
         cw[j] = 0;
         sb[j] = 0;
