@@ -280,6 +280,47 @@ def test_gather_matches_full_scan(fx, pl):
                     assert np.isneginf(ps[t, slot])
 
 
+@pytest.mark.parametrize("nq,max_blocks,stride", [(512, 1024, 1030), (256, 2100, 2100)])
+def test_gather_long_form_lists(fx, nq, max_blocks, stride):
+    """Launches of at least 2^22 slots (the prefill shape): one key cache shared by every query,
+    ragged lengths, unsorted block lists with duplicates, negative ids, ids past the range, counts
+    of zero, past max_blocks and negative. Every slot must equal the full scan's score of its
+    position bit for bit, or be -inf."""
+    n_keys = 20000
+    rng = np.random.default_rng(nq + max_blocks)
+    s = synth.signs(41)
+    keys = synth.normal_bf16(41, 3, 0, 0, n_keys * 128).reshape(n_keys, 128)
+    kc, ks = fx.idx_quantize_q(to_dev_bf16(keys), torch.from_numpy(s).cuda())
+    q = synth.normal_bf16(41, 2, 0, 0, nq * 32 * 128).reshape(nq, 32, 128)
+    qc, qs = fx.idx_quantize_q(to_dev_bf16(q), torch.from_numpy(s).cuda())
+    w = torch.from_numpy(synth.normal_f32(41, 4, 0, 0, nq * 32, 32 ** -0.5).reshape(nq, 32)).cuda()
+    n_vis = rng.integers(12000, n_keys + 1, nq).astype(np.int32)
+    n_vis[:3] = [0, 1, n_keys]
+    base = torch.zeros(nq, dtype=torch.int64, device="cuda")
+    nv = torch.from_numpy(n_vis).cuda()
+    scores = torch.full((nq, n_keys), float("nan"), device="cuda")
+    fx.idx_score_full(kc, ks, base, nv, qc, qs, w, n_keys, scores=scores)
+    nb_max = (n_keys + 7) // 8
+    blocks = rng.integers(-3, nb_max + 5, (nq, stride)).astype(np.int32)
+    blocks[1::3, :max_blocks // 2] = np.sort(rng.choice(nb_max, (len(blocks[1::3]), max_blocks // 2)), axis=1)
+    counts = rng.integers(0, max_blocks + 1, nq).astype(np.int32)
+    counts[3:9] = [0, max_blocks, max_blocks + 50, -4, 1, max_blocks - 1]
+    out = torch.full((nq, 8 * max_blocks + 16), float("nan"), device="cuda")
+    fx.idx_score_pool_gather(kc, ks, base, nv, torch.from_numpy(blocks).cuda(), torch.from_numpy(counts).cuda(),
+                             max_blocks, qc, qs, w, out)
+    torch.cuda.synchronize()
+    sc, got = scores.cpu().numpy(), out.cpu().numpy()
+    assert np.isnan(got[:, 8 * max_blocks:]).all()  # nothing written past the slots
+    got = got[:, :8 * max_blocks]
+    cnt = np.clip(counts, 0, max_blocks)
+    b = blocks[:, :max_blocks].astype(np.int64)
+    pos = (8 * b[:, :, None] + np.arange(8)).reshape(nq, -1)
+    ent = np.repeat(np.arange(max_blocks), 8)[None, :]
+    valid = (ent < cnt[:, None]) & (np.repeat(b, 8, axis=1) >= 0) & (pos < n_vis[:, None])
+    want = np.where(valid, sc[np.arange(nq)[:, None], np.where(valid, pos, 0)], -np.inf)
+    assert np.array_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32))
+
+
 def check_decode(fx, pl, wl, k=512):
     dev = pl.DeviceWorkload.from_workload(wl)
     out = pl.decode_step(dev, k=k)
