@@ -260,7 +260,8 @@ def bench_decode(wl, args) -> int:
     gb = pool_pos * 68 + wl.nq * (32 * 68 + 32 * 4) + slots * 4
     gather = {"kernel": "score_gather_kernel", "algorithmic_bytes_per_launch": gb,
               "ms_cold": gather_cold_ms, "hbm_frac_cold": gb / (gather_cold_ms / 1000.0) / 1e9 / HBM_PEAK_GBS,
-              "ms_warm": gather_warm_ms, "frac_warm": gb / (gather_warm_ms / 1000.0) / 1e9 / HBM_PEAK_GBS}
+              "ms_warm": gather_warm_ms, "frac_warm": gb / (gather_warm_ms / 1000.0) / 1e9 / HBM_PEAK_GBS,
+              "traffic": measured_traffic("score_gather_reindex_1m_traffic") if wl.name == "reindex_1m" else None}
     res = {
         "metric": "indexer entries scored/s + top-512 queries/s at 1M ctx; % of HBM roofline",
         "value": entries / (ms_step / 1000.0),
