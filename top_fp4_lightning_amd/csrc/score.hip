@@ -12,7 +12,10 @@
 // four lane rows are then combined for four tiles at once with two permlane32 swaps and one
 // permlane16 swap, which leaves the score of key l of the 64-key step in lane l.
 //
-// The next step's key loads stay in flight while the current step computes.
+// The four scale bytes of a step's key l arrive as one 32-bit load in lane l and reach the tile
+// lanes through ds_bpermute. The scan gives each wavefront one step (eight wavefronts per SIMD
+// keep the loads in flight); the gather's long form keeps the next step's loads in flight while
+// the current step computes.
 //
 // The scale-FP4 MFMA returns exact per-head dots whenever the per-block scale exponents of a
 // dot stay within a narrow range (exact sums of FP4 products below 2^24 ulps of the smallest
@@ -50,12 +53,33 @@ struct KTile {
     int sc;
 };
 
+// A 64-key step's operands: per tile u, this lane's 16 code bytes of key 16u + l % 16 (group
+// l / 16); and one 32-bit word per lane holding all four scale bytes of the step's key l. One
+// dword load per lane replaces four byte loads (one per tile) and leaves the memory pipeline a
+// quarter of the scale instructions; tile u's scale byte then comes from lane 16u + l % 16.
+struct KStep {
+    v4i b[4];
+    uint32_t sw;
+};
+
 template <int POLICY>
-__device__ __forceinline__ void load_key(const KeyRange& kr, uint32_t e, int g, KTile& kt) {
+__device__ __forceinline__ v4i load_codes(const KeyRange& kr, uint32_t e, int g) {
     const auto c =
         __builtin_amdgcn_raw_buffer_load_b128(kr.codes, e * (uint32_t)kRowBytes + (uint32_t)g * 16u, 0, POLICY);
-    kt.b = v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
-    kt.sc = (int)__builtin_amdgcn_raw_buffer_load_b8(kr.scales, e * (uint32_t)kGroups + (uint32_t)g, 0, POLICY);
+    return v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+}
+
+template <int POLICY>
+__device__ __forceinline__ uint32_t load_scale_word(const KeyRange& kr, uint32_t e) {
+    return __builtin_amdgcn_raw_buffer_load_b32(kr.scales, e * (uint32_t)kGroups, 0, POLICY);
+}
+
+// tile u of a step: the codes, and the scale byte of group g of key 16u + r taken from that key's lane
+__device__ __forceinline__ KTile step_tile(const KStep& ks, int u, int r, int g) {
+    KTile kt;
+    kt.b = ks.b[u];
+    kt.sc = (int)(((uint32_t)__builtin_amdgcn_ds_bpermute((16 * u + r) * 4, (int)ks.sw) >> (8 * g)) & 0xffu);
+    return kt;
 }
 
 struct TileOut {
@@ -112,21 +136,22 @@ __global__ __launch_bounds__(256) void score_full_kernel(ScoreArgs a) {
     float* bm_row = a.block_max ? a.block_max + t * a.bm_stride : nullptr;
     float* sc_row = a.scores ? a.scores + t * a.score_stride : nullptr;
 
-    KTile cur[4], nxt[4];
+    auto load_step = [&](int64_t e0, KStep& ks) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) load_key<kStream>(kr, (uint32_t)(e_begin + 16 * u + r), g, cur[u]);
+        for (int u = 0; u < 4; ++u) ks.b[u] = load_codes<kStream>(kr, (uint32_t)(e0 + 16 * u + r), g);
+        ks.sw = load_scale_word<kStream>(kr, (uint32_t)(e0 + lane));
+    };
+    KStep cur, nxt;
+    load_step(e_begin, cur);
     for (int it = 0; it < ITERS; ++it) {
         const int64_t e0 = e_begin + (int64_t)it * 64;
         if (e0 >= n) break;
-        if (it + 1 < ITERS) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) load_key<kStream>(kr, (uint32_t)(e0 + 64 + 16 * u + r), g, nxt[u]);
-        }
+        if (it + 1 < ITERS) load_step(e0 + 64, nxt);
         float p[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             TileOut o;
-            mfma_tile(q, cur[u], o);
+            mfma_tile(q, step_tile(cur, u, r, g), o);
             p[u] = lane_partial(q, o);
             if (a.head_dots) {
                 const int64_t e = e0 + 16 * u + r;
@@ -147,8 +172,7 @@ __global__ __launch_bounds__(256) void score_full_kernel(ScoreArgs a) {
             const float m = max8(valid ? s : -INFINITY);
             if ((lane & 7) == 0 && valid) bm_row[e >> 3] = m;
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+        cur = nxt;
     }
 }
 
@@ -194,24 +218,28 @@ __global__ __launch_bounds__(256) void score_gather_kernel(GatherArgs a) {
         }
     };
 
-    uint32_t pc[5], pn[5] = {kAbsent, kAbsent, kAbsent, kAbsent, kAbsent};
-    KTile cur[4], nxt[4];
-    step_positions(s_begin, pc);
+    // a lane's own slot (pos[4]) is slot 16u + r of tile u for the lanes that read its scale byte
+    auto load_step = [&](const uint32_t (&pos)[5], KStep& ks) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) load_key<kReuse>(kr, pc[u], g, cur[u]);
+        for (int u = 0; u < 4; ++u) ks.b[u] = load_codes<kReuse>(kr, pos[u], g);
+        ks.sw = load_scale_word<kReuse>(kr, pos[4]);
+    };
+    uint32_t pc[5], pn[5] = {kAbsent, kAbsent, kAbsent, kAbsent, kAbsent};
+    KStep cur, nxt;
+    step_positions(s_begin, pc);
+    load_step(pc, cur);
     for (int it = 0; it < ITERS; ++it) {
         const int64_t s0 = s_begin + (int64_t)it * 64;
         if (s0 >= slots) break;
         if (it + 1 < ITERS) {
             step_positions(s0 + 64, pn);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) load_key<kReuse>(kr, pn[u], g, nxt[u]);
+            load_step(pn, nxt);
         }
         float p[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             TileOut o;
-            mfma_tile(q, cur[u], o);
+            mfma_tile(q, step_tile(cur, u, r, g), o);
             p[u] = lane_partial(q, o);
             if (a.head_dots && pc[u] != kAbsent) {
                 const int64_t s = s0 + 16 * u + r;
@@ -225,14 +253,15 @@ __global__ __launch_bounds__(256) void score_gather_kernel(GatherArgs a) {
         const float sc = combine4(p[0], p[1], p[2], p[3]);
         const int64_t s = s0 + lane;
         if (s < slots) a.scores[t * a.score_stride + s] = pc[4] != kAbsent ? sc : -INFINITY;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+        cur = nxt;
 #pragma unroll
         for (int u = 0; u < 5; ++u) pc[u] = pn[u];
     }
 }
 
-constexpr int kScanIters = 4;    // 4 waves x 4 steps x 64 keys = 1024 keys per block
+// One 64-key step per wavefront (256 keys per block): the kernel then fits in 64 registers, eight
+// wavefronts per SIMD keep the most key loads in flight, and it streams at the rate of a plain read
+constexpr int kScanIters = 1;
 // Pool gather: one 64-slot step per wavefront when the launch is small (a decode step: the latency
 // of a few short-lived waves), several steps when it is large (prefill: the query is loaded once
 // per wavefront and the next step's keys are in flight while the current step computes).
