@@ -125,7 +125,7 @@ __device__ __forceinline__ uint32_t stage_chunk(int kk, int p) {
     return (uint32_t)(kk * 4 + (p ^ ((kk >> 1) & 3))) * 16u;
 }
 
-template <int QW, int KT, bool SCORES, bool BMAX>
+template <int QW, int KT, bool SCORES, bool BMAX, bool PARTIAL>
 __global__ __launch_bounds__(256, FP4IDX_MULTI_WAVES) void score_multi_kernel(ScoreArgs a) {
     __shared__ StageBuf sb;
     const int lane = threadIdx.x & 63;
@@ -150,13 +150,17 @@ __global__ __launch_bounds__(256, FP4IDX_MULTI_WAVES) void score_multi_kernel(Sc
         nb_max = n > nb_max ? n : nb_max;
     }
     if (e_begin >= nb_max) return;  // uniform per block
+    // queries of this wave inside the group: with PARTIAL (a group that is not a whole number of
+    // blocks) the last wave of a group may hold fewer than QW, or none (it still stages keys for the
+    // block but scores nothing); otherwise every wave holds QW and the check compiles away
+    const int qv = !PARTIAL ? QW : (int)(g_end - qw0 < 0 ? 0 : (g_end - qw0 < QW ? g_end - qw0 : QW));
     int nq_[QW];
     int nmax = 0, nmin = INT32_MAX;
 #pragma unroll
     for (int i = 0; i < QW; ++i) {
         nq_[i] = nvis(qw0 + i);
         nmax = nq_[i] > nmax ? nq_[i] : nmax;
-        nmin = nq_[i] < nmin ? nq_[i] : nmin;
+        if (i < qv) nmin = nq_[i] < nmin ? nq_[i] : nmin;
     }
     const int e_stop = e_begin + KT * kStepKeys < nb_max ? e_begin + KT * kStepKeys : nb_max;
     const int n_steps = (e_stop - e_begin + kStepKeys - 1) / kStepKeys;
@@ -229,6 +233,7 @@ __global__ __launch_bounds__(256, FP4IDX_MULTI_WAVES) void score_multi_kernel(Sc
         const bool flush = (it & 7) == 7 || it == last;  // uniform
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
+            if (i >= qv) break;  // uniform per wave
             const v16f o0 = mfma_tile32(q[i], t[0]);
             const v16f o1 = mfma_tile32(q[i], t[1]);
 #if FP4IDX_MULTI_ORDER == 1
@@ -299,12 +304,20 @@ hipError_t launch_score_multi(const ScoreArgs& a, hipStream_t stream) {
     const int64_t gy = (a.max_n + kMultiIters * 64 - 1) / (kMultiIters * 64);
     const int64_t gz = a.nq / a.group;
     const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)gz);
+    const bool partial = a.group % qtile != 0;
+    auto go = [&](auto scores, auto bmax) {
+        constexpr bool S = decltype(scores)::value, B = decltype(bmax)::value;
+        if (partial)
+            hipLaunchKernelGGL((score_multi_kernel<kMultiQ, kMultiIters, S, B, true>), grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((score_multi_kernel<kMultiQ, kMultiIters, S, B, false>), grid, dim3(256), 0, stream, a);
+    };
     if (a.scores && a.block_max)
-        hipLaunchKernelGGL((score_multi_kernel<kMultiQ, kMultiIters, true, true>), grid, dim3(256), 0, stream, a);
+        go(std::true_type{}, std::true_type{});
     else if (a.scores)
-        hipLaunchKernelGGL((score_multi_kernel<kMultiQ, kMultiIters, true, false>), grid, dim3(256), 0, stream, a);
+        go(std::true_type{}, std::false_type{});
     else
-        hipLaunchKernelGGL((score_multi_kernel<kMultiQ, kMultiIters, false, true>), grid, dim3(256), 0, stream, a);
+        go(std::false_type{}, std::true_type{});
     return hipGetLastError();
 }
 
