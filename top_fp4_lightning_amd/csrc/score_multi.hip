@@ -102,11 +102,12 @@ __device__ __forceinline__ float combine2(float p0, float p1) {
 }
 
 // Keys are staged in LDS once per block, two 64-key steps at a time: per step 4 KiB of codes
-// (16-byte chunks XOR-swizzled so that eight consecutive keys fall on distinct bank groups, both
-// for the staging writes and the operand reads) and 256 bytes of scales. Two buffers alternate;
-// one barrier per staged block orders the writes of block s + 1 before its reads and the reads
-// of block s - 1 before the buffer is overwritten. Control flow around the barriers is uniform
-// per block.
+// (16-byte chunks XOR-swizzled so that eight consecutive keys fall on distinct bank groups for
+// the operand reads) and 256 bytes of scales. The staging uses direct-to-LDS buffer loads (no
+// registers in between), three buffers deep: while block s is scored, the loads of blocks s + 1
+// and s + 2 are in flight. One barrier per staged block, after each wave has waited for its own
+// loads of block s, publishes block s and frees the buffer of block s - 1 for the next issue.
+// Control flow around the barriers is uniform per block.
 //
 // Block maxima: after a step, all eight lanes of a key block hold its maximum; lane 8g + s keeps
 // block g of step s (mod 8) in one register per query, and every eighth step (or at the wave's
@@ -114,18 +115,32 @@ __device__ __forceinline__ float combine2(float p0, float p1) {
 constexpr int kStepKeys = 64;
 constexpr int kStageSteps = 2;                      // 64-key steps per staged block (one barrier)
 constexpr int kStageCodes = kStepKeys * kRowBytes;  // bytes of codes per step
+#ifndef FP4IDX_MULTI_BUFS
+#define FP4IDX_MULTI_BUFS 3
+#endif
+constexpr int kBufs = FP4IDX_MULTI_BUFS;  // staged blocks in LDS: kBufs - 1 in flight while one is scored
 
 struct StageBuf {
-    alignas(16) uint8_t codes[2][kStageSteps][kStageCodes];
-    alignas(16) uint32_t scales[2][kStageSteps * kStepKeys];
+    alignas(16) uint8_t codes[kBufs][kStageSteps][kStageCodes];
+    alignas(16) uint32_t scales[kBufs][kStageSteps * kStepKeys];
 };
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// wait until at most N of this wave's vector-memory loads are outstanding (loads complete in
+// order, so every load issued before the last N has landed, in LDS for the direct loads)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // LDS byte offset of 16-byte chunk p (0..3) of key kk (0..63) of a step
 __device__ __forceinline__ uint32_t stage_chunk(int kk, int p) {
     return (uint32_t)(kk * 4 + (p ^ ((kk >> 1) & 3))) * 16u;
 }
 
-template <int QW, int KT, bool SCORES, bool BMAX, bool PARTIAL>
+template <int QW, int KT, bool SCORES, bool BMAX>
 __global__ __launch_bounds__(256, FP4IDX_MULTI_WAVES) void score_multi_kernel(ScoreArgs a) {
     __shared__ StageBuf sb;
     const int lane = threadIdx.x & 63;
@@ -150,10 +165,9 @@ __global__ __launch_bounds__(256, FP4IDX_MULTI_WAVES) void score_multi_kernel(Sc
         nb_max = n > nb_max ? n : nb_max;
     }
     if (e_begin >= nb_max) return;  // uniform per block
-    // queries of this wave inside the group: with PARTIAL (a group that is not a whole number of
-    // blocks) the last wave of a group may hold fewer than QW, or none (it still stages keys for the
-    // block but scores nothing); otherwise every wave holds QW and the check compiles away
-    const int qv = !PARTIAL ? QW : (int)(g_end - qw0 < 0 ? 0 : (g_end - qw0 < QW ? g_end - qw0 : QW));
+    // queries of this wave inside the group: the last wave of a group may hold fewer than QW, or
+    // none (it still stages keys for the block but scores nothing)
+    const int qv = (int)(g_end - qw0 < 0 ? 0 : (g_end - qw0 < QW ? g_end - qw0 : QW));
     int nq_[QW];
     int nmax = 0, nmin = INT32_MAX;
 #pragma unroll
@@ -181,28 +195,27 @@ __global__ __launch_bounds__(256, FP4IDX_MULTI_WAVES) void score_multi_kernel(Sc
         brow[i] = BMAX ? a.block_max + qq * a.bm_stride : nullptr;
     }
 
-    // staging: for every step of a staged block, thread T carries 16-byte chunk T % 4 of key
-    // T / 4; threads below 128 also carry one scale word
-    const int T = threadIdx.x;
-    const uint32_t st_code = stage_chunk(T >> 2, T & 3);
-    v4i st_c[kStageSteps];
-    uint32_t st_s = 0;
-    auto stage_load = [&](int sg) {
+    // Staging with direct-to-LDS loads: lane l of a wave's load lands at the instruction's LDS base
+    // + 16 l (4 l for a word), so each lane fetches the global chunk that belongs at its LDS slot.
+    // Per staged block every wave issues kStageSteps + 1 loads: for each step its 1 KiB of the
+    // codes (slots 64 wave .. 64 wave + 63, i.e. keys 16 wave .. 16 wave + 15, with the XOR swizzle
+    // undone on the global side), and the 64 scale words of step wave % 2 (waves 2 and 3 repeat
+    // waves 0 and 1 with the same bytes, so that all waves count the same loads).
+    constexpr int kLoadsPerStage = kStageSteps + 1;
+    auto stage_issue = [&](int sg) {
+        const int buf = sg % kBufs;
         const uint32_t e0 = (uint32_t)(e_begin + sg * kStageSteps * kStepKeys);
-#pragma unroll
-        for (int ss = 0; ss < kStageSteps; ++ss) {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-                kr.codes, (e0 + ss * kStepKeys) * kRowBytes + (uint32_t)T * 16u, 0, kReuse);
-            st_c[ss] = v4i{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
-        }
-        if (T < kStageSteps * kStepKeys)
-            st_s = __builtin_amdgcn_raw_buffer_load_b32(kr.scales, (e0 + (uint32_t)T) * kGroups, 0, kReuse);
-    };
-    auto stage_store = [&](int buf) {
+        const int slot = 64 * wave + lane;
+        const int kk = slot >> 2;
+        const int p = (slot & 3) ^ ((kk >> 1) & 3);
 #pragma unroll
         for (int ss = 0; ss < kStageSteps; ++ss)
-            *reinterpret_cast<v4i*>(__builtin_assume_aligned(&sb.codes[buf][ss][st_code], 16)) = st_c[ss];
-        if (T < kStageSteps * kStepKeys) sb.scales[buf][T] = st_s;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                kr.codes, (lds_void_ptr)&sb.codes[buf][ss][1024 * wave], 16,
+                (e0 + (uint32_t)(ss * kStepKeys + kk)) * kRowBytes + (uint32_t)p * 16u, 0, 0, kReuse);
+        const int ss = wave & 1;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr.scales, (lds_void_ptr)&sb.scales[buf][ss * kStepKeys], 4,
+                                                 (e0 + (uint32_t)(ss * kStepKeys + lane)) * kGroups, 0, 0, kReuse);
     };
     // operands of tile u (keys 32u .. 32u + 31) of step ss of buffer buf
     auto read_tiles = [&](int buf, int ss, KTile32 (&t)[2]) {
@@ -261,26 +274,33 @@ __global__ __launch_bounds__(256, FP4IDX_MULTI_WAVES) void score_multi_kernel(Sc
     };
 
     const int n_stages = (n_steps + kStageSteps - 1) / kStageSteps;
-    stage_load(0);
-    stage_store(0);
-    if (n_stages > 1) stage_load(1);
-    __syncthreads();
+    for (int sg = 0; sg < kBufs - 1 && sg < n_stages; ++sg) stage_issue(sg);
+#pragma nounroll
     for (int sg = 0; sg < n_stages; ++sg) {
+        // staged blocks issued after this one so far: their loads may stay in flight
+        const int younger = (n_stages - 1 < sg + kBufs - 2 ? n_stages - 1 : sg + kBufs - 2) - sg;
+        if (kBufs >= 4 && younger >= 2)
+            wait_vm<2 * kLoadsPerStage>();
+        else if (younger >= 1)
+            wait_vm<kLoadsPerStage>();
+        else
+            wait_vm<0>();
+        // every wave's loads of block sg have landed, and every wave is done with block sg - 1,
+        // whose buffer the next issue overwrites
+        __syncthreads();
+        if (sg + kBufs - 1 < n_stages) stage_issue(sg + kBufs - 1);
 #pragma unroll
         for (int ss = 0; ss < kStageSteps; ++ss) {
             const int it = sg * kStageSteps + ss;
             if (it <= last) {  // uniform per wave
                 KTile32 t[2];
-                read_tiles(sg & 1, ss, t);
+                read_tiles(sg % kBufs, ss, t);
                 if (e_begin + (it + 1) * kStepKeys <= nmin)
                     step(t, it, std::false_type{});
                 else
                     step(t, it, std::true_type{});
             }
         }
-        if (sg + 1 < n_stages) stage_store((sg + 1) & 1);
-        if (sg + 2 < n_stages) stage_load(sg + 2);
-        __syncthreads();
     }
 }
 
@@ -304,20 +324,12 @@ hipError_t launch_score_multi(const ScoreArgs& a, hipStream_t stream) {
     const int64_t gy = (a.max_n + kMultiIters * 64 - 1) / (kMultiIters * 64);
     const int64_t gz = a.nq / a.group;
     const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)gz);
-    const bool partial = a.group % qtile != 0;
-    auto go = [&](auto scores, auto bmax) {
-        constexpr bool S = decltype(scores)::value, B = decltype(bmax)::value;
-        if (partial)
-            hipLaunchKernelGGL((score_multi_kernel<kMultiQ, kMultiIters, S, B, true>), grid, dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL((score_multi_kernel<kMultiQ, kMultiIters, S, B, false>), grid, dim3(256), 0, stream, a);
-    };
     if (a.scores && a.block_max)
-        go(std::true_type{}, std::true_type{});
+        hipLaunchKernelGGL((score_multi_kernel<kMultiQ, kMultiIters, true, true>), grid, dim3(256), 0, stream, a);
     else if (a.scores)
-        go(std::true_type{}, std::false_type{});
+        hipLaunchKernelGGL((score_multi_kernel<kMultiQ, kMultiIters, true, false>), grid, dim3(256), 0, stream, a);
     else
-        go(std::false_type{}, std::true_type{});
+        hipLaunchKernelGGL((score_multi_kernel<kMultiQ, kMultiIters, false, true>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
