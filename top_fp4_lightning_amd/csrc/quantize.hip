@@ -10,21 +10,59 @@
 namespace fp4idx {
 namespace {
 
-__device__ __forceinline__ double shfl_xor16(double v, int m) { return __shfl_xor(v, m, 16); }
-__device__ __forceinline__ float shfl_xor16f(float v, int m) { return __shfl_xor(v, m, 16); }
+// Partner exchange inside each 16-lane row through the data-parallel-primitive network (a few
+// cycles, no LDS round trip): the value of lane li ^ M. M = 1, 2: quad permutations; M = 8: a
+// rotation of the row by 8; M = 4: a shift by 4 up or down, chosen by the lane's bit 2.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane32(uint32_t v, int li) {
+    if constexpr (M == 1) return dpp32<0xB1>(v);   // quad_perm [1,0,3,2]
+    if constexpr (M == 2) return dpp32<0x4E>(v);   // quad_perm [2,3,0,1]
+    if constexpr (M == 8) return dpp32<0x128>(v);  // row_ror:8
+    if constexpr (M == 4) {
+        const uint32_t up = dpp32<0x104>(v);  // row_shl:4, the value of lane li + 4
+        const uint32_t dn = dpp32<0x114>(v);  // row_shr:4, the value of lane li - 4
+        return (li & 4) ? dn : up;
+    }
+    return v;
+}
+template <int M>
+__device__ __forceinline__ double xor_lane(double v, int li) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = xor_lane32<M>((uint32_t)b, li), hi = xor_lane32<M>((uint32_t)(b >> 32), li);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+template <int M>
+__device__ __forceinline__ float xor_lanef(float v, int li) {
+    return __uint_as_float(xor_lane32<M>(__float_as_uint(v), li));
+}
 
 // E2M1 code (0..7) of a magnitude v in [0, 6]: nearest grid value, ties to even mantissa
-__device__ __forceinline__ uint32_t e2m1_mag_code(double a) {
+__device__ __forceinline__ uint32_t e2m1_mag_code(float a) {
     uint32_t c;
-    if (a <= 0.25) c = 0;
-    else if (a < 0.75) c = 1;
-    else if (a <= 1.25) c = 2;
-    else if (a < 1.75) c = 3;
-    else if (a <= 2.5) c = 4;
-    else if (a < 3.5) c = 5;
-    else if (a <= 5.0) c = 6;
+    if (a <= 0.25f) c = 0;
+    else if (a < 0.75f) c = 1;
+    else if (a <= 1.25f) c = 2;
+    else if (a < 1.75f) c = 3;
+    else if (a <= 2.5f) c = 4;
+    else if (a < 3.5f) c = 5;
+    else if (a <= 5.0f) c = 6;
     else c = 7;
     return c;
+}
+
+// one butterfly stage over element-index bit 8 M (lane bit M)
+template <int M>
+__device__ __forceinline__ void lane_stage(double (&v)[8], int li) {
+    const bool upper = (li & M) != 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const double p = xor_lane<M>(v[i], li);
+        v[i] = upper ? (p - v[i]) : (v[i] + p);
+    }
 }
 
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t rows,
@@ -32,7 +70,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
                                                        uint8_t* __restrict__ scales) {
     const int li = threadIdx.x & 15;
     const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const bool live = row < rows;  // dead lanes still join the shuffles of their 16-lane group
+    const bool live = row < rows;  // dead lanes still join the lane exchanges of their 16-lane group
 
     uint4 raw = make_uint4(0u, 0u, 0u, 0u);
     if (live) raw = *reinterpret_cast<const uint4*>(x + row * kDim + li * 8);
@@ -61,15 +99,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
         }
     }
     // butterflies over element-index bits 8, 16, 32, 64 (lane bits 1, 2, 4, 8)
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-        const bool upper = (li & m) != 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            double p = shfl_xor16(v[i], m);
-            v[i] = upper ? (p - v[i]) : (v[i] + p);
-        }
-    }
+    lane_stage<1>(v, li);
+    lane_stage<2>(v, li);
+    lane_stage<4>(v, li);
+    lane_stage<8>(v, li);
     const float inv = 0x1.6a09e6p-4f;  // fl32(2^-3.5)
     float y[8];
     float amax = 0.0f;
@@ -80,23 +113,24 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
         amax = fmaxf(amax, fabsf(y[i]));
     }
     // group of 32 = 4 consecutive lanes
-    amax = fmaxf(amax, shfl_xor16f(amax, 1));
-    amax = fmaxf(amax, shfl_xor16f(amax, 2));
+    amax = fmaxf(amax, xor_lanef<1>(amax, li));
+    amax = fmaxf(amax, xor_lanef<2>(amax, li));
 
     int e = -127;
-    const double ad = (double)amax;
-    if (ad > 0.0) {
+    if (amax > 0.0f) {
         int E;
-        double m = frexp(ad, &E);  // ad = m * 2^E, 0.5 <= m < 1
-        e = (m <= 0.75) ? E - 3 : E - 2;
+        const float m = frexpf(amax, &E);  // amax = m * 2^E, 0.5 <= m < 1 (exact, subnormals too)
+        e = (m <= 0.75f) ? E - 3 : E - 2;
         e = e < -127 ? -127 : (e > 127 ? 127 : e);
     }
+    // y / 2^e in fp32: exact whenever the result is at least 2^-126, and a smaller magnitude
+    // encodes to 0 however it rounds; |y / 2^e| <= 6 by the choice of e
     uint32_t packed = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        double vd = ldexp((double)y[i], -e);
-        uint32_t c = e2m1_mag_code(fabs(vd));
-        if (c != 0 && vd < 0.0) c |= 8u;
+        const float vd = ldexpf(y[i], -e);
+        uint32_t c = e2m1_mag_code(fabsf(vd));
+        if (c != 0 && vd < 0.0f) c |= 8u;
         packed |= c << (4 * i);
     }
     if (live) {
