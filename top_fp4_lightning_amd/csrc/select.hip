@@ -841,12 +841,50 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(SelectArg
     const uint32_t k = (uint32_t)a.k;
     const uint64_t* gc = ws.cand + t * ws.cap;
     const uint64_t* L = gc;
+    const RowInfo ri = row_info(a, t);
+    // pool ids leave through an LDS bitmap of the row's blocks: cleared before the first barrier
+    const bool bitmap = a.pool_mode && ri.len <= kBitmapMax;
+    const int words = bitmap ? (int)((ri.len + 31) / 32) : 0;
+    for (int i = threadIdx.x; i < words; i += kFinishThreads) bits[i] = 0u;
     if (C <= (uint32_t)kFinishCap) {
         for (uint32_t i = threadIdx.x; i < C; i += kFinishThreads) list[i] = gc[i];
         L = list;
     }
     __syncthreads();
     const uint64_t T = C > k ? list_radix<kFinishThreads>(L, C, k, T0, hist, S) : 1ull;
+    if (bitmap) {
+        // the winners are the entries at or above T: exactly min(C, k) of them, since T is the
+        // k-th largest of distinct composites (or 1, every entry, when C <= k)
+        for (uint32_t i = threadIdx.x; i < C; i += kFinishThreads) {
+            const uint64_t x = entry_composite(L[i]);
+            if (x >= T) {
+                const uint32_t pos = comp_pos(x);
+                atomicOr(&bits[pos >> 5], 1u << (pos & 31));
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) ws.st[t].n_cand = 0u;  // cleared for the next call
+        // ascending block ids through the bitmap and a block-wide prefix sum
+        const int per = (words + kFinishThreads - 1) / kFinishThreads;
+        const int w0 = threadIdx.x * per;
+        uint32_t mine = 0;
+        for (int q = 0; q < per; ++q)
+            if (w0 + q < words) mine += (uint32_t)__popc(bits[w0 + q]);
+        uint32_t nall;
+        uint32_t base = block_scan<kFinishThreads>(mine, S.wsum[0], nall);
+        for (int q = 0; q < per; ++q) {
+            if (w0 + q >= words) break;
+            uint32_t b = bits[w0 + q];
+            while (b) {
+                const int bit = __ffs(b) - 1;
+                b &= b - 1;
+                a.out_idx[t * a.out_stride + base] = (w0 + q) * 32 + bit;
+                ++base;
+            }
+        }
+        write_pad(a, t, C < k ? C : k);
+        return;
+    }
     // the winners, gathered in rounds of 8 consecutive entries per thread
     constexpr int Q = 8;
     uint32_t nw = 0;
@@ -877,35 +915,7 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(SelectArg
     __syncthreads();
     if (threadIdx.x == 0) ws.st[t].n_cand = 0u;  // cleared for the next call
     const uint32_t cnt = nw < k ? nw : k;
-    const RowInfo ri = row_info(a, t);
-    if (a.pool_mode && ri.len <= kBitmapMax) {
-        // ascending block ids through an LDS bitmap and a block-wide prefix sum
-        const int words = (int)((ri.len + 31) / 32);
-        for (int i = threadIdx.x; i < words; i += kFinishThreads) bits[i] = 0u;
-        __syncthreads();
-        for (uint32_t i = threadIdx.x; i < cnt; i += kFinishThreads) {
-            const uint32_t pos = comp_pos(out[i]);
-            atomicOr(&bits[pos >> 5], 1u << (pos & 31));
-        }
-        __syncthreads();
-        const int per = (words + kFinishThreads - 1) / kFinishThreads;
-        const int w0 = threadIdx.x * per;
-        uint32_t mine = 0;
-        for (int q = 0; q < per; ++q)
-            if (w0 + q < words) mine += (uint32_t)__popc(bits[w0 + q]);
-        uint32_t nall;
-        uint32_t base = block_scan<kFinishThreads>(mine, S.wsum[0], nall);
-        for (int q = 0; q < per; ++q) {
-            if (w0 + q >= words) break;
-            uint32_t b = bits[w0 + q];
-            while (b) {
-                const int bit = __ffs(b) - 1;
-                b &= b - 1;
-                a.out_idx[t * a.out_stride + base] = (w0 + q) * 32 + bit;
-                ++base;
-            }
-        }
-    } else {
+    {
         // ascending position: sort (pos, key) pairs
         int N = 1;
         while (N < (int)cnt) N <<= 1;
