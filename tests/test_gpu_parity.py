@@ -402,7 +402,7 @@ def test_topk_with_block_map(fx, nblocks, k):
 
 @pytest.mark.parametrize("outputs", ["both", "block_max", "scores"])
 @pytest.mark.parametrize("n_keys,nqs,group", [(6000, 48, 48), (3000, 37, 37), (20000, 70, 35), (9000, 16, 16),
-                                              # groups that run three-wave blocks
+                                              # groups that leave query slots of the last block of a group empty
                                               (7000, 30, 6), (5000, 10, 5), (3000, 9, 3), (12000, 36, 6)])
 def test_multi_query_scan_matches_single_query(fx, pl, n_keys, nqs, group, outputs):
     # the many-query scan (group > 1) must reproduce the per-query scan bit for bit, for each
