@@ -7,12 +7,6 @@
 namespace fp4idx {
 namespace {
 
-#ifndef FP4IDX_MULTI_WAVES
-#define FP4IDX_MULTI_WAVES 1
-#endif
-#ifndef FP4IDX_MULTI_ORDER
-#define FP4IDX_MULTI_ORDER 0
-#endif
 // Many queries sharing one key range (chunked prefill, speculative decode).
 //
 // Work unit: a tile of 32 keys against all 32 heads of one query as two
@@ -141,7 +135,7 @@ __device__ __forceinline__ uint32_t stage_chunk(int kk, int p) {
 }
 
 template <int QW, int KT, bool SCORES, bool BMAX>
-__global__ __launch_bounds__(256, FP4IDX_MULTI_WAVES) void score_multi_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(256) void score_multi_kernel(ScoreArgs a) {
     __shared__ StageBuf sb;
     const int lane = threadIdx.x & 63;
     // wave index as a uniform value: query bounds, key range and descriptors stay scalar
@@ -249,9 +243,6 @@ __global__ __launch_bounds__(256, FP4IDX_MULTI_WAVES) void score_multi_kernel(Sc
             if (i >= qv) break;  // uniform per wave
             const v16f o0 = mfma_tile32(q[i], t[0]);
             const v16f o1 = mfma_tile32(q[i], t[1]);
-#if FP4IDX_MULTI_ORDER == 1
-            __builtin_amdgcn_sched_barrier(0);
-#endif
             const float sc = combine2(lane_partial32(q[i], o0), lane_partial32(q[i], o1));
             const bool valid = !MASKED || el < nq_[i];
             if (SCORES && valid) srow[i][el] = sc;
@@ -267,9 +258,7 @@ __global__ __launch_bounds__(256, FP4IDX_MULTI_WAVES) void score_multi_kernel(Sc
             }
             // one query's matrix results live at a time: keeps the wave within the register
             // budget of four waves per SIMD (other waves hide the matrix latency)
-#if FP4IDX_MULTI_ORDER != 2
             __builtin_amdgcn_sched_barrier(0);
-#endif
         }
     };
 
