@@ -4,7 +4,8 @@
 // in fp64 (every partial sum of bf16 inputs is exact), then fl32(S) * fl32(2^-3.5) in fp32.
 // Scale: smallest e with 6 * 2^e >= group max (the ideal max/6 rounded up to a power of two).
 // Codes: E2M1 by threshold comparison on y / 2^e (nearest, ties to the even mantissa bit).
-// Layout: 16 lanes per row, lane i owns elements 8i .. 8i+7; 16 rows per 256-thread block.
+// Layout: 16 lanes per row (lane i owns elements 8i .. 8i+7), or 32 lanes per row (elements
+// 4i .. 4i+3) for small launches.
 #include "internal.h"
 
 namespace fp4idx {
@@ -26,6 +27,12 @@ __device__ __forceinline__ uint32_t xor_lane32(uint32_t v, int li) {
         const uint32_t up = dpp32<0x104>(v);  // row_shl:4, the value of lane li + 4
         const uint32_t dn = dpp32<0x114>(v);  // row_shr:4, the value of lane li - 4
         return (li & 4) ? dn : up;
+    }
+    if constexpr (M == 16) {
+        // swap of neighbouring 16-lane rows: the first result holds rows (0, 0, 2, 2), the
+        // second rows (1, 1, 3, 3)
+        const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (li & 16) ? sw[0] : sw[1];
     }
     return v;
 }
@@ -54,43 +61,61 @@ __device__ __forceinline__ uint32_t e2m1_mag_code(float a) {
     return c;
 }
 
-// one butterfly stage over element-index bit 8 M (lane bit M)
-template <int M>
-__device__ __forceinline__ void lane_stage(double (&v)[8], int li) {
+// one butterfly stage over lane bit M (element-index bit M * EPL)
+template <int M, int EPL>
+__device__ __forceinline__ void lane_stage(double (&v)[EPL], int li) {
     const bool upper = (li & M) != 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < EPL; ++i) {
         const double p = xor_lane<M>(v[i], li);
         v[i] = upper ? (p - v[i]) : (v[i] + p);
     }
 }
 
+// LPR lanes per row, EPL = 128 / LPR consecutive elements per lane: 16 lanes (8 elements) for
+// large launches (fewer instructions per row), 32 lanes (4 elements) for small ones (query rows
+// of a decode step: half the dependent work per lane, so a shorter path through the kernel).
+template <int LPR>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                        const int8_t* __restrict__ signs, uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales) {
-    const int li = threadIdx.x & 15;
-    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const bool live = row < rows;  // dead lanes still join the lane exchanges of their 16-lane group
+    constexpr int EPL = kDim / LPR;      // elements per lane
+    constexpr int GL = 32 / EPL;         // lanes per 32-element scale group
+    const int li = threadIdx.x & (LPR - 1);
+    const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + (threadIdx.x / LPR);
+    const bool live = row < rows;  // dead lanes still join the lane exchanges of their row group
 
-    uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-    if (live) raw = *reinterpret_cast<const uint4*>(x + row * kDim + li * 8);
-    const uint2 sg = *reinterpret_cast<const uint2*>(signs + li * 8);
-    const uint32_t words[4] = {raw.x, raw.y, raw.z, raw.w};
-    const uint32_t sw[2] = {sg.x, sg.y};
+    uint32_t words[EPL / 2] = {};
+    uint32_t sw[EPL / 4];
+    if constexpr (EPL == 8) {
+        if (live) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(x + row * kDim + li * 8);
+            words[0] = raw.x; words[1] = raw.y; words[2] = raw.z; words[3] = raw.w;
+        }
+        const uint2 sg = *reinterpret_cast<const uint2*>(signs + li * 8);
+        sw[0] = sg.x;
+        sw[1] = sg.y;
+    } else {
+        if (live) {
+            const uint2 raw = *reinterpret_cast<const uint2*>(x + row * kDim + li * 4);
+            words[0] = raw.x; words[1] = raw.y;
+        }
+        sw[0] = *reinterpret_cast<const uint32_t*>(signs + li * 4);
+    }
 
-    double v[8];
+    double v[EPL];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < EPL; ++i) {
         uint32_t h = (i & 1) ? (words[i >> 1] >> 16) : (words[i >> 1] & 0xffffu);
         float f = __uint_as_float(h << 16);
         int s = (int)(int8_t)((sw[i >> 2] >> (8 * (i & 3))) & 0xffu);
         v[i] = (double)f * (double)s;
     }
-    // butterflies over element-index bits 1, 2, 4 (inside the lane)
+    // butterflies over the element-index bits inside the lane
 #pragma unroll
-    for (int b = 1; b < 8; b <<= 1) {
+    for (int b = 1; b < EPL; b <<= 1) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < EPL; ++i) {
             if (!(i & b)) {
                 double p = v[i], q = v[i | b];
                 v[i] = p + q;
@@ -98,23 +123,25 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
             }
         }
     }
-    // butterflies over element-index bits 8, 16, 32, 64 (lane bits 1, 2, 4, 8)
-    lane_stage<1>(v, li);
-    lane_stage<2>(v, li);
-    lane_stage<4>(v, li);
-    lane_stage<8>(v, li);
+    // butterflies over the lane bits (element-index bits EPL .. 64)
+    lane_stage<1, EPL>(v, li);
+    lane_stage<2, EPL>(v, li);
+    lane_stage<4, EPL>(v, li);
+    lane_stage<8, EPL>(v, li);
+    if constexpr (LPR == 32) lane_stage<16, EPL>(v, li);
     const float inv = 0x1.6a09e6p-4f;  // fl32(2^-3.5)
-    float y[8];
+    float y[EPL];
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < EPL; ++i) {
         float s32 = (float)v[i];
         y[i] = s32 * inv;
         amax = fmaxf(amax, fabsf(y[i]));
     }
-    // group of 32 = 4 consecutive lanes
+    // group of 32 = GL consecutive lanes
     amax = fmaxf(amax, xor_lanef<1>(amax, li));
     amax = fmaxf(amax, xor_lanef<2>(amax, li));
+    if constexpr (GL == 8) amax = fmaxf(amax, xor_lanef<4>(amax, li));
 
     int e = -127;
     if (amax > 0.0f) {
@@ -127,25 +154,38 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     // encodes to 0 however it rounds; |y / 2^e| <= 6 by the choice of e
     uint32_t packed = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < EPL; ++i) {
         const float vd = ldexpf(y[i], -e);
         uint32_t c = e2m1_mag_code(fabsf(vd));
         if (c != 0 && vd < 0.0f) c |= 8u;
         packed |= c << (4 * i);
     }
     if (live) {
-        *reinterpret_cast<uint32_t*>(codes + row * kRowBytes + li * 4) = packed;
-        if ((li & 3) == 0) scales[row * kGroups + (li >> 2)] = (uint8_t)(e + 127);
+        if constexpr (EPL == 8)
+            *reinterpret_cast<uint32_t*>(codes + row * kRowBytes + li * 4) = packed;
+        else
+            *reinterpret_cast<uint16_t*>(codes + row * kRowBytes + li * 2) = (uint16_t)packed;
+        if (li % GL == 0) scales[row * kGroups + li / GL] = (uint8_t)(e + 127);
     }
 }
+
+// launches up to this many rows take the 32-lane form
+constexpr int64_t kSmallQuantRows = 4096;
 
 }  // namespace
 
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, const int8_t* signs, uint8_t* codes, uint8_t* scales,
                            hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
-    const int64_t blocks = (rows + 15) / 16;
-    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, signs, codes, scales);
+    if (rows <= kSmallQuantRows) {
+        const int64_t blocks = (rows + 7) / 8;
+        hipLaunchKernelGGL(quantize_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, signs, codes,
+                           scales);
+    } else {
+        const int64_t blocks = (rows + 15) / 16;
+        hipLaunchKernelGGL(quantize_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, signs, codes,
+                           scales);
+    }
     return hipGetLastError();
 }
 
