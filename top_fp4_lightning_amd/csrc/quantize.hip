@@ -4,8 +4,8 @@
 // in fp64 (every partial sum of bf16 inputs is exact), then fl32(S) * fl32(2^-3.5) in fp32.
 // Scale: smallest e with 6 * 2^e >= group max (the ideal max/6 rounded up to a power of two).
 // Codes: E2M1 by threshold comparison on y / 2^e (nearest, ties to the even mantissa bit).
-// Layout: 16 lanes per row (lane i owns elements 8i .. 8i+7), or 32 lanes per row (elements
-// 4i .. 4i+3) for small launches.
+// Layout: 16 lanes per row (lane i owns elements 8i .. 8i+7), or a wavefront per row (elements
+// 2i, 2i+1) for small launches.
 #include "internal.h"
 
 namespace fp4idx {
@@ -27,6 +27,11 @@ __device__ __forceinline__ uint32_t xor_lane32(uint32_t v, int li) {
         const uint32_t up = dpp32<0x104>(v);  // row_shl:4, the value of lane li + 4
         const uint32_t dn = dpp32<0x114>(v);  // row_shr:4, the value of lane li - 4
         return (li & 4) ? dn : up;
+    }
+    if constexpr (M == 32) {
+        // swap of the two 32-lane halves: the first result holds (low, low), the second (high, high)
+        const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (li & 32) ? sw[0] : sw[1];
     }
     if constexpr (M == 16) {
         // swap of neighbouring 16-lane rows: the first result holds rows (0, 0, 2, 2), the
@@ -73,8 +78,9 @@ __device__ __forceinline__ void lane_stage(double (&v)[EPL], int li) {
 }
 
 // LPR lanes per row, EPL = 128 / LPR consecutive elements per lane: 16 lanes (8 elements) for
-// large launches (fewer instructions per row), 32 lanes (4 elements) for small ones (query rows
-// of a decode step: half the dependent work per lane, so a shorter path through the kernel).
+// large launches (fewer instructions per row), 64 lanes (2 elements) for small ones (the query
+// rows of a decode step: the least dependent work per lane, so the shortest path through the
+// kernel).
 template <int LPR>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                        const int8_t* __restrict__ signs, uint8_t* __restrict__ codes,
@@ -86,7 +92,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     const bool live = row < rows;  // dead lanes still join the lane exchanges of their row group
 
     uint32_t words[EPL / 2] = {};
-    uint32_t sw[EPL / 4];
+    uint32_t sw[EPL >= 4 ? EPL / 4 : 1];
     if constexpr (EPL == 8) {
         if (live) {
             const uint4 raw = *reinterpret_cast<const uint4*>(x + row * kDim + li * 8);
@@ -95,12 +101,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
         const uint2 sg = *reinterpret_cast<const uint2*>(signs + li * 8);
         sw[0] = sg.x;
         sw[1] = sg.y;
-    } else {
+    } else if constexpr (EPL == 4) {
         if (live) {
             const uint2 raw = *reinterpret_cast<const uint2*>(x + row * kDim + li * 4);
             words[0] = raw.x; words[1] = raw.y;
         }
         sw[0] = *reinterpret_cast<const uint32_t*>(signs + li * 4);
+    } else {
+        if (live) words[0] = *reinterpret_cast<const uint32_t*>(x + row * kDim + li * 2);
+        sw[0] = *reinterpret_cast<const uint16_t*>(signs + li * 2);
     }
 
     double v[EPL];
@@ -128,7 +137,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     lane_stage<2, EPL>(v, li);
     lane_stage<4, EPL>(v, li);
     lane_stage<8, EPL>(v, li);
-    if constexpr (LPR == 32) lane_stage<16, EPL>(v, li);
+    if constexpr (LPR >= 32) lane_stage<16, EPL>(v, li);
+    if constexpr (LPR >= 64) lane_stage<32, EPL>(v, li);
     const float inv = 0x1.6a09e6p-4f;  // fl32(2^-3.5)
     float y[EPL];
     float amax = 0.0f;
@@ -141,7 +151,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     // group of 32 = GL consecutive lanes
     amax = fmaxf(amax, xor_lanef<1>(amax, li));
     amax = fmaxf(amax, xor_lanef<2>(amax, li));
-    if constexpr (GL == 8) amax = fmaxf(amax, xor_lanef<4>(amax, li));
+    if constexpr (GL >= 8) amax = fmaxf(amax, xor_lanef<4>(amax, li));
+    if constexpr (GL >= 16) amax = fmaxf(amax, xor_lanef<8>(amax, li));
 
     int e = -127;
     if (amax > 0.0f) {
@@ -163,14 +174,18 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     if (live) {
         if constexpr (EPL == 8)
             *reinterpret_cast<uint32_t*>(codes + row * kRowBytes + li * 4) = packed;
-        else
+        else if constexpr (EPL == 4)
             *reinterpret_cast<uint16_t*>(codes + row * kRowBytes + li * 2) = (uint16_t)packed;
+        else
+            codes[row * kRowBytes + li] = (uint8_t)packed;
         if (li % GL == 0) scales[row * kGroups + li / GL] = (uint8_t)(e + 127);
     }
 }
 
-// launches up to this many rows take the 32-lane form
+// launches up to this many rows take a whole wavefront per row (two elements per lane: the
+// shortest path through the kernel; 32 lanes per row measured 1.5 us slower per decode step)
 constexpr int64_t kSmallQuantRows = 4096;
+constexpr int kSmallQuantLanes = 64;
 
 }  // namespace
 
@@ -178,8 +193,9 @@ hipError_t launch_quantize(const uint16_t* x, int64_t rows, const int8_t* signs,
                            hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
     if (rows <= kSmallQuantRows) {
-        const int64_t blocks = (rows + 7) / 8;
-        hipLaunchKernelGGL(quantize_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, signs, codes,
+        constexpr int L = kSmallQuantLanes;
+        const int64_t blocks = (rows + 256 / L - 1) / (256 / L);
+        hipLaunchKernelGGL(quantize_kernel<L>, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, signs, codes,
                            scales);
     } else {
         const int64_t blocks = (rows + 15) / 16;
