@@ -57,16 +57,6 @@ struct KTile32 {
     int sc;
 };
 
-__device__ __forceinline__ void load_key32(const KeyRange& kr, uint32_t e, int h, KTile32& kt) {
-    const uint32_t off = e * (uint32_t)kRowBytes + (uint32_t)h * 32u;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const auto c = __builtin_amdgcn_raw_buffer_load_b128(kr.codes, off + 16u * k, 0, kReuse);
-        kt.b[k] = v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
-    }
-    kt.sc = (int)__builtin_amdgcn_raw_buffer_load_b16(kr.scales, e * (uint32_t)kGroups + (uint32_t)h * 2u, 0, kReuse);
-}
-
 __device__ __forceinline__ v16f mfma_tile32(const QRegs32& q, const KTile32& kt) {
     v16f z;
 #pragma unroll
