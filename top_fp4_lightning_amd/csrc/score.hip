@@ -186,35 +186,43 @@ __global__ __launch_bounds__(256) void score_gather_kernel(GatherArgs a) {
     const int64_t t = blockIdx.y;
     const int64_t slots = (int64_t)a.max_blocks * kBlock;
     const int64_t s_begin = ((int64_t)blockIdx.x * 4 + wave) * (ITERS * 64);
-    if (s_begin >= slots) return;
+    const int g = lane >> 4, r = lane & 15;
+    const int32_t* blk = a.blocks + t * a.blocks_stride;
+
+    // Block ids of one 64-slot step: the four tiles' slots of this lane and the lane's own output
+    // slot, read unconditionally (clamped to the row) so that the four key loads of a step are
+    // issued back to back instead of each waiting on its own id. The first step's ids and the
+    // query need only the kernel arguments and are requested before the query's count and
+    // length, so that the kernel's start is two memory round trips before the key loads, not
+    // three. (Waves past the slots, in the last block, run with every slot absent and store
+    // nothing.)
+    auto step_ids = [&](int64_t s0, int32_t (&b)[5]) {
+#pragma unroll
+        for (int u = 0; u < 5; ++u) {
+            const int64_t i = (s0 + (u < 4 ? 16 * u + r : lane)) >> 3;
+            b[u] = blk[i < a.max_blocks ? i : a.max_blocks - 1];
+        }
+    };
+    int32_t bc[5];
+    step_ids(s_begin, bc);
+    QRegs q;
+    load_query(a.q_codes, a.q_scales, a.w, t, lane, q);
     int64_t cnt = a.block_count[t];
     cnt = cnt < 0 ? 0 : (cnt > a.max_blocks ? a.max_blocks : cnt);
     int64_t n = a.n_vis[t];
     n = n < 0 ? 0 : (n > kMaxScanKeys ? kMaxScanKeys : n);
-
-    QRegs q;
-    load_query(a.q_codes, a.q_scales, a.w, t, lane, q);
     const KeyRange kr = key_range(a.k_codes, a.k_scales, a.k_base[t], n);
-    const int g = lane >> 4, r = lane & 15;
-    const int32_t* blk = a.blocks + t * a.blocks_stride;
 
-    // Key indices of one 64-slot step: the four tiles' slots of this lane and the lane's own
-    // output slot. The block ids are read first, all five unconditionally (clamped to the row), so
-    // that the key loads of the four tiles are issued back to back instead of each waiting on its
-    // own id; absent slots (past the count or the row, negative ids, positions >= n) map to kAbsent.
-    auto step_positions = [&](int64_t s0, uint32_t (&pos)[5]) {
-        int32_t b[5];
-#pragma unroll
-        for (int u = 0; u < 5; ++u) {
-            const int64_t s = s0 + (u < 4 ? 16 * u + r : lane);
-            const int64_t i = s >> 3;
-            b[u] = blk[i < a.max_blocks ? i : a.max_blocks - 1];
-        }
+    // key indices of a step's slots; absent slots (past the slots, the count or the row, negative
+    // ids, positions >= n) map to kAbsent
+    auto step_positions = [&](int64_t s0, const int32_t (&b)[5], uint32_t (&pos)[5]) {
 #pragma unroll
         for (int u = 0; u < 5; ++u) {
             const int64_t s = s0 + (u < 4 ? 16 * u + r : lane);
             const int64_t e = (int64_t)b[u] * kBlock + (s & 7);
-            pos[u] = (s < slots && (s >> 3) < cnt && b[u] >= 0 && e < n) ? (uint32_t)e : kAbsent;
+            // bitwise, not short-circuit: no branch for the compiler to sink the id loads into
+            const bool ok = (s < slots) & ((s >> 3) < cnt) & (b[u] >= 0) & (e < n);
+            pos[u] = ok ? (uint32_t)e : kAbsent;
         }
     };
 
@@ -226,13 +234,15 @@ __global__ __launch_bounds__(256) void score_gather_kernel(GatherArgs a) {
     };
     uint32_t pc[5], pn[5] = {kAbsent, kAbsent, kAbsent, kAbsent, kAbsent};
     KStep cur, nxt;
-    step_positions(s_begin, pc);
+    step_positions(s_begin, bc, pc);
     load_step(pc, cur);
     for (int it = 0; it < ITERS; ++it) {
         const int64_t s0 = s_begin + (int64_t)it * 64;
         if (s0 >= slots) break;
         if (it + 1 < ITERS) {
-            step_positions(s0 + 64, pn);
+            int32_t bn[5];
+            step_ids(s0 + 64, bn);
+            step_positions(s0 + 64, bn, pn);
             load_step(pn, nxt);
         }
         float p[4];
