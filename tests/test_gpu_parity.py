@@ -361,15 +361,18 @@ def test_decode_ragged_batch(fx, pl):
     check_decode(fx, pl, synth.decode_workload("r", 203, [20001, 5000, 700, 16384, 16385, 9], layers=2))
 
 
-def test_prefill_parity(fx, pl):
-    wl = synth.prefill_workload("pf", 204, 6000, 48)
-    dev = pl.DeviceWorkload.from_workload(wl, group=48)
+@pytest.mark.parametrize("n_keys,nq", [(6000, 48), (4100, 8), (700, 64), (300, 20)])
+def test_prefill_parity(fx, pl, n_keys, nq):
+    # chunked prefill end to end; the small caches leave queries with fewer than 512 blocks (every
+    # block kept) and, at 300 keys, fewer than 512 visible keys (all of them selected, then -1)
+    wl = synth.prefill_workload("pf", 204 + n_keys, n_keys, nq)
+    dev = pl.DeviceWorkload.from_workload(wl, group=nq)
     plan = pl.PrefillPlan(dev).run()
     torch.cuda.synchronize()
     top = plan.topk.cpu().numpy()
     s = wl.signs()
     kc, ks = oracle.quantize(wl.keys(0), s)
-    for t in range(0, wl.nq, 5):
+    for t in list(range(0, wl.nq, 5)) + [wl.nq - 1]:
         n = int(wl.n_vis[t])
         qc, qs = oracle.quantize(wl.q(0, [t])[0], s)
         I, A = oracle.score_rows(qc, qs, wl.w(0, [t])[0], kc[:n], ks[:n])
