@@ -361,6 +361,12 @@ def test_decode_ragged_batch(fx, pl):
     check_decode(fx, pl, synth.decode_workload("r", 203, [20001, 5000, 700, 16384, 16385, 9], layers=2))
 
 
+def test_decode_ragged_batch_long_pool(fx, pl):
+    # rows past 16384 blocks send the whole batch's pool through the long-row selection (bound,
+    # collect, finish), short and empty rows included
+    check_decode(fx, pl, synth.decode_workload("rl", 207, [300000, 9, 0, 140000, 131073, 1000], layers=1))
+
+
 @pytest.mark.parametrize("n_keys,nq", [(6000, 48), (4100, 8), (700, 64), (300, 20)])
 def test_prefill_parity(fx, pl, n_keys, nq):
     # chunked prefill end to end; the small caches leave queries with fewer than 512 blocks (every
