@@ -152,6 +152,15 @@ def test_spec_decode_1m(pl):
     check_decode_queries(wl, out, sample=[0, 5, 46])
 
 
+def test_spec_decode_ragged(pl):
+    # speculative verification over ragged sequences: a sequence of exactly 6 keys (its positions
+    # see 1 .. 6), short ones, and one past 16384 blocks, so that every pool of the batch goes
+    # through the long-row selection; every position checked
+    wl = synth.spec_decode_workload("sps", 215, [6, 700, 20001, 140000], positions=6, layers=2)
+    out = run_decode(pl, wl)
+    check_decode_queries(wl, out, sample=list(range(wl.nq)))
+
+
 def test_token_1m_encoder_layers(pl):
     # the per-token schedule: 3 encoder Full layers over their own 8 x 2^19 caches, then the
     # decoder step; sampled encoder queries against the oracle (the decoder part is
