@@ -47,7 +47,7 @@ def test_quantize_kv_matches_oracle(fx):
     assert np.array_equal(codes.cpu().numpy(), want_c)
 
 
-@pytest.mark.parametrize("nq,k", [(1, 1), (3, 512), (37, 100)])
+@pytest.mark.parametrize("nq,k", [(1, 1), (3, 512), (37, 100), (5, 7), (2, 1500)])
 def test_gather_kv_matches_oracle(fx, nq, k):
     rng = np.random.default_rng(nq * 1000 + k)
     rows_per_seq = 2000
