@@ -93,9 +93,30 @@ __device__ __forceinline__ void hist_clear_own(Hist<NT>& H) {
     for (int i = 0; i < kHistBins / 2 / 64; ++i) H.hw[w][l + 64 * i] = 0u;
 }
 
+// Histogram increments from the active lanes of a wavefront. When every active lane hits the
+// same bin (rows of ties, or a pass over bits the candidates share) one lane adds the count:
+// same-address atomics from a whole wavefront would otherwise serialise.
 template <int NT>
 __device__ __forceinline__ void hist_add(Hist<NT>& H, uint32_t digit) {
-    atomicAdd(&H.hw[threadIdx.x >> 6][digit >> 1], 1u << (16 * (digit & 1)));
+    uint32_t* hw = H.hw[threadIdx.x >> 6];
+    const uint64_t act = __ballot(1);
+    const uint32_t d0 = __builtin_amdgcn_readfirstlane(digit);
+    if (__ballot(digit == d0) == act) {
+        if ((uint32_t)(threadIdx.x & 63) == (uint32_t)(__ffsll((unsigned long long)act) - 1))
+            atomicAdd(&hw[d0 >> 1], (uint32_t)__popcll(act) << (16 * (d0 & 1)));
+    } else {
+        atomicAdd(&hw[digit >> 1], 1u << (16 * (digit & 1)));
+    }
+}
+
+__device__ __forceinline__ void bin_add(uint32_t* h, uint32_t bin) {
+    const uint64_t act = __ballot(1);
+    const uint32_t b0 = __builtin_amdgcn_readfirstlane(bin);
+    if (__ballot(bin == b0) == act) {
+        if ((uint32_t)(threadIdx.x & 63) == (uint32_t)(__ffsll((unsigned long long)act) - 1)) atomicAdd(&h[b0], (uint32_t)__popcll(act));
+    } else {
+        atomicAdd(&h[bin], 1u);
+    }
 }
 
 template <int NT>
@@ -481,7 +502,7 @@ __device__ uint64_t list_radix(const uint64_t* L, uint32_t C, uint32_t k, uint32
         uint32_t* h = hist + (pass & 1) * kHistBins;
         for (uint32_t i = tid; i < C; i += NT) {
             const uint64_t x = entry_composite(L[i]);
-            if (((x ^ prefix) & mask) == 0 && x < lim) atomicAdd(&h[(x >> lo) & dm], 1u);
+            if (((x ^ prefix) & mask) == 0 && x < lim) bin_add(h, (uint32_t)((x >> lo) & dm));
         }
         __syncthreads();
         // every thread is past the previous pass's reads of the other histogram: clear it for
