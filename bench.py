@@ -294,11 +294,12 @@ def bench_decode(wl, args) -> int:
 
 def bench_mask_form(args) -> int:
     """The decode step at fullscan_1m in the pool's training form, all 5 layers batched: one
-    many-query scan writes every layer's full score row (8 x 5 rows of 2^20), then the pool, the
-    mask and a top-512 per row ("DeepSeek-V4.1 model structure (3)", sections "three details of
-    the pool in the code" and "the pool also acts in training"). The gather form (the inference
-    step of bench_decode) is timed beside it on the same resident inputs; both give the same
-    selections. The roofline is the scan's FP4 matrix rate."""
+    many-query scan writes every layer's full score row (8 x 5 rows of 2^20), then the pool and a
+    top-512 per row over its query's pooled positions ("DeepSeek-V4.1 model structure (3)",
+    sections "three details of the pool in the code" and "the pool also acts in training"). Timed
+    beside it on the same resident inputs: the literal form (the mask written in place, then a
+    top-512 over whole rows) and the gather form (the inference step of bench_decode); all three
+    give the same selections. The roofline is the scan's FP4 matrix rate."""
     import numpy as np
     import torch
 
@@ -309,6 +310,7 @@ def bench_mask_form(args) -> int:
     t = time.perf_counter()
     dev = pipeline.DeviceWorkload.from_workload(wl)
     mask = pipeline.MaskFormPlan(dev)
+    literal = pipeline.MaskFormPlan(dev, write_mask=True)
     gather = pipeline.DecodePlan(dev)
     torch.cuda.synchronize()
     log(f"mask_form_1m: {wl.nq} queries x {mask.L} layers, {wl.total_keys} keys; setup {time.perf_counter() - t:.1f} s")
@@ -328,6 +330,8 @@ def bench_mask_form(args) -> int:
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     ms_mask = timed(mask_step, args.steps, evs)
     scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    timed(lambda e: literal.run(), args.warmup)
+    ms_literal = timed(lambda e: literal.run(), args.steps)
     timed(lambda e: gather.run(), args.warmup)
     ms_gather = timed(lambda e: gather.run(), args.steps)
     n_vis = [int(x) for x in wl.n_vis]
@@ -342,10 +346,12 @@ def bench_mask_form(args) -> int:
         "vs_baseline": None, "dtype": "mxfp4",
         "data": "synthetic (seeded N(0,1) bf16 q/k, N(0,1/32) w, 1% planted keys; no trained weights)",
         "config": {"workload": "mask_form_1m: 8 x 1048576 keys, Full + 4 Reindex layers each scoring every "
-                               "position in one many-query scan, pool mask, top-512 per layer", "batch": wl.nseq,
+                               "position in one many-query scan, pool, top-512 per layer over the pooled "
+                               "positions", "batch": wl.nseq,
                    "layers": mask.L, "k": 512, "pool_blocks": 2048, "block": 8},
         "top512_queries_per_s": mask.rows / (ms_mask / 1000.0),
         "scan_ms": scan_ms,
+        "mask_written_ms_per_step": ms_literal,
         "gather_form_ms_per_step": ms_gather,
         "mask_over_gather": ms_mask / ms_gather,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -232,6 +232,35 @@ idx_status idx_mask_pool(float* scores, int64_t score_stride, const int32_t* n_v
                          int32_t block, void* stream);
 
 /*
+ * idx_topk_pool: the top-k of full score rows restricted to the candidate pool ([P1] "three details
+ * of the pool in the code": a layer's scores outside the pooled blocks count as -inf before its
+ * top-512). The result equals idx_mask_pool followed by idx_topk on the same rows, but the rows
+ * are read only at the pooled positions and left unchanged. With p = t / group, row t's
+ * candidates are the positions 8 * pool_blocks[p][i] + r (i < min(pool_count[p], max_blocks),
+ * r < 8) below n_t; ids outside [0, ceil(n_t / 8)) contribute nothing. Ranking, ties and the -1 /
+ * -inf padding are those of idx_topk; indices are absolute positions, in ascending order when
+ * the block ids are ascending and distinct (as idx_build_pool writes them); a repeated id would
+ * report its positions twice.
+ *
+ *   scores       : device fp32 [nq][score_stride], score_stride >= max_n (read only).
+ *   n_vis, max_n : device int32 [nq]; n_t = min(max(n_vis[t], 0), max_n); max_n 0 .. 2^28.
+ *   pool_blocks  : device int32 [nq / group][pool_stride]; pool_count: device int32 [nq / group].
+ *   max_blocks   : 0 .. 2048, <= pool_stride: the pool width read (one block of threads per row).
+ *   group        : >= 1 and divides nq (rows of several layers of one query share its pool).
+ *   block        : must be 8.
+ *   k            : 1 .. 2048.
+ *   out_idx      : device int32 [nq][out_stride], out_stride >= k; out_val: fp32, same shape, or NULL.
+ * No workspace: every row is handled by one block of threads in LDS.
+ * Errors: IDX_EINVAL (null pointer, a stride too small, group not dividing nq), IDX_EALIGN
+ * (pointers not 4-byte aligned), IDX_EUNSUPPORTED (k, nq, max_n, max_blocks out of range,
+ * block != 8); nothing is launched on error. nq == 0 is a no-op.
+ */
+idx_status idx_topk_pool(const float* scores, int64_t score_stride, const int32_t* n_vis, int32_t nq, int64_t max_n,
+                         const int32_t* pool_blocks, int64_t pool_stride, const int32_t* pool_count,
+                         int32_t max_blocks, int32_t group, int32_t block, int32_t k, int32_t* out_idx,
+                         int64_t out_stride, float* out_val, void* stream);
+
+/*
  * Main-KV FP4 storage ([P1] "the scale format decides precision" and "removing the global scale
  * still leaves enough range"): a main-KV entry is 512 values stored as E2M1 codes (element 2i in
  * the low nibble of byte i) with one E4M3 scale per group of 16 values and no global scale,

@@ -36,7 +36,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["idx_quantize_q", "idx_score_full", "idx_build_pool", "idx_score_pool_gather", "idx_topk",
-              "idx_last_error", "idx_abi_version", "idx_workspace_size", "idx_quantize_kv", "idx_gather_kv", "idx_mask_pool"]:
+              "idx_last_error", "idx_abi_version", "idx_workspace_size", "idx_quantize_kv", "idx_gather_kv", "idx_mask_pool",
+              "idx_topk_pool"]:
         assert n in names
 
 
@@ -190,6 +191,32 @@ def test_mask_pool_validation(fx):
     assert m(*bad) == fx.IDX_EUNSUPPORTED
     bad = list(good); bad[0] = FAKE + 2
     assert m(*bad) == fx.IDX_EALIGN
+
+
+def test_topk_pool_validation(fx):
+    m = lambda *a: call(fx, "idx_topk_pool", *a)[0]
+    # scores, stride, n_vis, nq, max_n, pool_blocks, pool_stride, pool_count, max_blocks, group, block, k,
+    # out_idx, out_stride, out_val, stream
+    good = [FAKE, 4096, FAKE, 10, 4096, FAKE, 2048, FAKE, 512, 5, 8, 512, FAKE, 512, None, None]
+    empty = list(good); empty[3] = 0
+    assert m(*empty) == fx.IDX_OK  # no rows: a no-op
+    for i, v, st in [(0, None, fx.IDX_EINVAL), (2, None, fx.IDX_EINVAL), (5, None, fx.IDX_EINVAL),
+                     (7, None, fx.IDX_EINVAL), (12, None, fx.IDX_EINVAL),
+                     (1, 100, fx.IDX_EINVAL),  # score_stride < max_n
+                     (6, 511, fx.IDX_EINVAL),  # pool_stride < max_blocks
+                     (13, 511, fx.IDX_EINVAL),  # out_stride < k
+                     (9, 3, fx.IDX_EINVAL), (9, 0, fx.IDX_EINVAL),  # group must divide nq
+                     (11, 0, fx.IDX_EUNSUPPORTED), (11, 2049, fx.IDX_EUNSUPPORTED),
+                     (8, 2049, fx.IDX_EUNSUPPORTED), (8, -1, fx.IDX_EUNSUPPORTED),
+                     (4, (1 << 28) + 1, fx.IDX_EUNSUPPORTED), (10, 16, fx.IDX_EUNSUPPORTED),
+                     (0, FAKE + 2, fx.IDX_EALIGN), (14, FAKE + 2, fx.IDX_EALIGN)]:
+        bad = list(good)
+        bad[i] = v
+        if i == 4:
+            bad[1] = v
+        assert m(*bad) == st, (i, v)
+    bad = list(good); bad[3] = 70000; bad[9] = 1
+    assert m(*bad) == fx.IDX_EUNSUPPORTED
 
 
 def test_python_binding_refuses_cpu_tensors(fx):

@@ -106,20 +106,23 @@ def test_fullscan_1m(pl):
 
 
 def test_mask_form_fullscan_1m(pl):
-    # the training form at the benchmark's workload: every layer scores all 2^20 positions, the
-    # pool masks them; pools and every layer's top-512 equal the gather form's (whose selections
-    # test_fullscan_1m pins to the oracle)
+    # the training form at the benchmark's workload: every layer scores all 2^20 positions and
+    # keeps the pooled ones (top-512 over the pooled positions, and the literal in-place mask with
+    # a top-512 over whole rows); pools and every layer's top-512 equal the gather form's (whose
+    # selections test_fullscan_1m pins to the oracle)
     wl = synth.config("fullscan_1m")
     dev = pl.DeviceWorkload.from_workload(wl)
     gather = pl.DecodePlan(dev).run()
-    mask = pl.MaskFormPlan(dev).run()
-    torch.cuda.synchronize()
-    assert torch.equal(mask.pool_count, gather.pool_count)
-    assert torch.equal(mask.pool_blocks, gather.pool_blocks)
-    for layer in range(mask.L):
-        mi, mv = mask.layer_topk(layer)
-        assert torch.equal(mi, gather.topk[layer]), f"layer {layer}"
-        assert torch.equal(mv, gather.topk_val[layer]), f"layer {layer}"
+    for write_mask in (False, True):
+        mask = pl.MaskFormPlan(dev, write_mask=write_mask).run()
+        torch.cuda.synchronize()
+        assert torch.equal(mask.pool_count, gather.pool_count)
+        assert torch.equal(mask.pool_blocks, gather.pool_blocks)
+        for layer in range(mask.L):
+            mi, mv = mask.layer_topk(layer)
+            assert torch.equal(mi, gather.topk[layer]), f"layer {layer} write_mask={write_mask}"
+            assert torch.equal(mv, gather.topk_val[layer]), f"layer {layer} write_mask={write_mask}"
+        del mask
 
 
 def test_fullscan_512k(pl):

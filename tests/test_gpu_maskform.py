@@ -72,10 +72,99 @@ def test_mask_pool_bit_exact(fx, n_vis, max_n, group):
         assert np.array_equal(got[t, n:], before[t, n:].cpu().numpy()), f"row {t}: past n_vis must not change"
 
 
-def check_mask_equals_gather(pl, wl):
+def topk_pool_case(seed, n_vis, max_n, group, max_blocks, pool_stride, ties):
+    """Seeded rows (optionally few distinct values with -0 among them, so that ties decide) and one
+    pool per `group` rows: distinct block ids, some outside the row, ascending in even pools and
+    shuffled in odd ones, counts that run into the -1 padding or past max_blocks."""
+    rng = np.random.default_rng(seed)
+    nq = len(n_vis)
+    rows = rng.standard_normal((nq, max_n + 3)).astype(np.float32)
+    if ties:
+        rows = (np.round(rows * 2) / 2).astype(np.float32)
+    npool = nq // group
+    pools = np.full((npool, pool_stride), -1, dtype=np.int32)
+    counts = np.zeros(npool, dtype=np.int32)
+    for p in range(npool):
+        nb = (max(int(max(n_vis[p * group: (p + 1) * group])), 1) + 7) // 8
+        span = np.arange(-3, nb + 5, dtype=np.int32)
+        c = int(rng.integers(0, min(pool_stride, len(span)) + 1))
+        ids = rng.choice(span, size=c, replace=False).astype(np.int32)
+        if p % 2 == 0:
+            ids.sort()
+        pools[p, :c] = ids
+        counts[p] = c + (7 if p % 3 == 0 else 0)
+    return rows, pools, counts
+
+
+@pytest.mark.parametrize("n_vis,max_n,group,max_blocks,k,ties", [
+    ([1000, 0, 8, 9, 16384, 16385, 40000, 50000], 50000, 1, 2048, 512, False),
+    ([70000, 69999, 65536, 1], 70000, 2, 2048, 512, True),
+    ([5, 300000, 12, 8], 300000, 4, 2048, 512, False),
+    ([3000, 2001, 777, 64], 3000, 1, 100, 300, True),  # narrow pool, counts past max_blocks clamp
+    ([20000, 19999], 20000, 1, 2048, 2048, False),  # k = 2048: more than half of a full pool
+    ([33, 100], 90, 2, 16, 7, False),  # n_vis above max_n clamps to it
+])
+def test_topk_pool_against_oracle(fx, n_vis, max_n, group, max_blocks, k, ties):
+    """idx_topk_pool is the oracle's mask-then-top-k: same positions (ascending for ascending
+    pools), the scores at them, -1 / -inf after them."""
+    rows, pools, counts = topk_pool_case(len(n_vis) * 11 + group + k, n_vis, max_n, group, max_blocks,
+                                         max(max_blocks, 64), ties)
+    nq = len(n_vis)
+    d = torch.from_numpy(rows).cuda()
+    nv = torch.tensor(n_vis, dtype=torch.int32, device="cuda")
+    out = torch.full((nq, k + 5), 77, dtype=torch.int32, device="cuda")
+    val = torch.full((nq, k + 5), 77.0, dtype=torch.float32, device="cuda")
+    fx.idx_topk_pool(d, nv, max_n, torch.from_numpy(pools).cuda(), torch.from_numpy(counts).cuda(), max_blocks, k,
+                     out, out_val=val, group=group)
+    torch.cuda.synchronize()
+    got, gv = out.cpu().numpy(), val.cpu().numpy()
+    assert (got[:, k:] == 77).all() and (gv[:, k:] == 77.0).all(), "wrote past k"
+    for t, n in enumerate(n_vis):
+        n = min(n, max_n)
+        p = t // group
+        ids = pools[p, :min(int(counts[p]), max_blocks)]
+        ref = oracle.reindex_mask(rows[t, :n].astype(np.float64), ids, 8, k)
+        want = [int(x) for x in ref if x >= 0]
+        sel = [int(x) for x in got[t, :k] if x >= 0]
+        what = f"row {t} n={n} pool {p} ({len(ids)} ids)"
+        assert len(sel) == len(want), what
+        assert (got[t, len(sel):k] == -1).all() and np.isneginf(gv[t, len(sel):k]).all(), what
+        if p % 2 == 0:
+            assert sel == sorted(want), what
+        else:
+            assert sorted(sel) == sorted(want), what
+        v = rows[t, sel] + np.float32(0.0)  # a selected -0 is reported as +0
+        assert np.array_equal(gv[t, :len(sel)].view(np.uint32), v.view(np.uint32)), what
+
+
+def test_topk_pool_equals_mask_then_topk(fx):
+    """The fused call and the literal form (in-place mask, then a top-k over whole rows, the long-row
+    path) give the same bits, on rows longer than one selection block."""
+    n_vis = [200000, 131073, 16385, 90000]
+    max_n = 200000
+    rows, pools, counts = topk_pool_case(5, n_vis, max_n, 2, 2048, 2048, False)
+    pools = np.sort(np.where(pools < 0, np.iinfo(np.int32).max, pools), axis=1)  # ascending, padding last
+    pools[pools == np.iinfo(np.int32).max] = -1
+    d = torch.from_numpy(rows).cuda()
+    nv = torch.tensor(n_vis, dtype=torch.int32, device="cuda")
+    pb, pc = torch.from_numpy(pools).cuda(), torch.from_numpy(counts).cuda()
+    o1 = torch.empty(4, 512, dtype=torch.int32, device="cuda")
+    v1 = torch.empty(4, 512, dtype=torch.float32, device="cuda")
+    fx.idx_topk_pool(d, nv, max_n, pb, pc, 2048, 512, o1, out_val=v1, group=2)
+    fx.idx_mask_pool(d, nv, max_n, pb, pc, group=2)
+    o2 = torch.empty_like(o1)
+    v2 = torch.empty_like(v1)
+    ws = fx.workspace(fx.IDX_OP_TOPK, 4, max_n, 512)
+    fx.idx_topk(d, max_n, 512, o2, ws, n_valid=nv, out_val=v2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(v1.view(torch.int32), v2.view(torch.int32))
+
+
+def check_mask_equals_gather(pl, wl, write_mask=False):
     dev = pl.DeviceWorkload.from_workload(wl)
     gather = pl.DecodePlan(dev).run()
-    mask = pl.MaskFormPlan(dev).run()
+    mask = pl.MaskFormPlan(dev, write_mask=write_mask).run()
     torch.cuda.synchronize()
     assert torch.equal(mask.pool_count, gather.pool_count)
     for t in range(dev.nq):
@@ -88,9 +177,10 @@ def check_mask_equals_gather(pl, wl):
         assert torch.equal(mv[sel], gather.topk_val[layer][sel]), f"layer {layer} top-k values"
 
 
-def test_mask_form_equals_gather_form_ragged(fx, pl):
+@pytest.mark.parametrize("write_mask", [False, True])
+def test_mask_form_equals_gather_form_ragged(fx, pl, write_mask):
     check_mask_equals_gather(pl, synth.decode_workload("mf", 211, [20001, 5000, 700, 16384, 16385, 9, 40000],
-                                                       layers=3))
+                                                       layers=3), write_mask)
 
 
 def test_mask_form_equals_gather_form_spec_decode(fx, pl):

@@ -37,13 +37,14 @@ lib.idx_topk.argtypes = [_P, _i64, _P, _i32, _i64, _i32, _P, _i64, _i32, _P, _i6
 lib.idx_quantize_kv.argtypes = [_P, _i64, _P, _P, _P]
 lib.idx_gather_kv.argtypes = [_P, _P, _P, _P, _i32, _P, _i64, _i32, _P, _P]
 lib.idx_mask_pool.argtypes = [_P, _i64, _P, _i32, _i64, _P, _i64, _P, _i32, _i32, _P]
+lib.idx_topk_pool.argtypes = [_P, _i64, _P, _i32, _i64, _P, _i64, _P, _i32, _i32, _i32, _i32, _P, _i64, _P, _P]
 for _f in ("idx_quantize_q", "idx_score_full", "idx_build_pool", "idx_score_pool_gather", "idx_topk",
-           "idx_quantize_kv", "idx_gather_kv", "idx_mask_pool"):
+           "idx_quantize_kv", "idx_gather_kv", "idx_mask_pool", "idx_topk_pool"):
     getattr(lib, _f).restype = _i32
 
 EXPORTS = ("idx_abi_version", "idx_last_error", "idx_workspace_size", "idx_quantize_q", "idx_score_full",
            "idx_build_pool", "idx_score_pool_gather", "idx_topk", "idx_quantize_kv", "idx_gather_kv",
-           "idx_mask_pool")
+           "idx_mask_pool", "idx_topk_pool")
 MKV_DIM = 512
 
 
@@ -211,3 +212,17 @@ def idx_mask_pool(scores, n_vis, max_n: int, pool_blocks, pool_count, group: int
     _check(lib.idx_mask_pool(_rows_ptr(scores), scores.stride(0), _ptr(n_vis), nq, max_n, _rows_ptr(pool_blocks),
                              pool_blocks.stride(0), _ptr(pool_count), group, block, _stream(stream)))
     return scores
+
+
+def idx_topk_pool(scores, n_vis, max_n: int, pool_blocks, pool_count, max_blocks: int, k: int, out_idx,
+                  out_val=None, group: int = 1, block: int = BLOCK, stream=None):
+    """Top-k of full score rows over the pooled positions only (equal to idx_mask_pool then
+    idx_topk, without writing the mask); score row t uses pool row t // group."""
+    _need(scores, torch.float32, "scores")
+    _need(pool_blocks, torch.int32, "pool_blocks")
+    _need(out_idx, torch.int32, "out_idx")
+    nq = n_vis.shape[0]
+    _check(lib.idx_topk_pool(_rows_ptr(scores), scores.stride(0), _ptr(n_vis), nq, max_n, _rows_ptr(pool_blocks),
+                             pool_blocks.stride(0), _ptr(pool_count), max_blocks, group, block, k, _ptr(out_idx),
+                             out_idx.stride(0), _ptr(out_val), _stream(stream)))
+    return out_idx, out_val

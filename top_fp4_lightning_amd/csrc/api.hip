@@ -43,6 +43,7 @@ idx_status hip_status(hipError_t e, const char* what) {
 constexpr int64_t kMaxRows = (int64_t)1 << 36;
 constexpr int64_t kMaxN = (int64_t)1 << 30;
 constexpr int32_t kMaxQueries = 65535;  // grid y dimension
+constexpr int64_t kMaxPoolScoreN = (int64_t)1 << 28;  // a score row read through a pool: below 2^30 bytes
 
 size_t ws_bytes_for(int32_t op, int32_t nq, int64_t max_n, int32_t k) {
     if (nq < 0 || max_n < 0 || max_n > kMaxN || k < 1 || k > kMaxK) return 0;
@@ -199,6 +200,51 @@ idx_status idx_topk(const float* scores, int64_t score_stride, const int32_t* n_
     return hip_status(launch_select(a, (hipStream_t)stream), "idx_topk");
 }
 
+idx_status idx_topk_pool(const float* scores, int64_t score_stride, const int32_t* n_vis, int32_t nq, int64_t max_n,
+                         const int32_t* pool_blocks, int64_t pool_stride, const int32_t* pool_count,
+                         int32_t max_blocks, int32_t group, int32_t block, int32_t k, int32_t* out_idx,
+                         int64_t out_stride, float* out_val, void* stream) {
+    REQUIRE(k >= 1 && k <= kMaxK, IDX_EUNSUPPORTED, "idx_topk_pool: k=%d out of [1, 2048]", k);
+    REQUIRE(nq >= 0 && nq <= kMaxQueries, IDX_EUNSUPPORTED, "idx_topk_pool: nq=%d out of [0, 65535]", nq);
+    REQUIRE(max_n >= 0 && max_n <= kMaxPoolScoreN, IDX_EUNSUPPORTED, "idx_topk_pool: max_n=%lld out of [0, 2^28]",
+            (long long)max_n);
+    REQUIRE(block == kBlock, IDX_EUNSUPPORTED, "idx_topk_pool: block=%d (only 8 is implemented)", block);
+    REQUIRE(max_blocks >= 0 && max_blocks <= kMaxK, IDX_EUNSUPPORTED, "idx_topk_pool: max_blocks=%d out of [0, 2048]",
+            max_blocks);
+    REQUIRE(group >= 1 && (nq == 0 || nq % group == 0), IDX_EINVAL, "idx_topk_pool: group=%d must divide nq=%d",
+            group, nq);
+    if (nq == 0) return ok();
+    REQUIRE(scores && n_vis && pool_blocks && pool_count && out_idx, IDX_EINVAL, "idx_topk_pool: null pointer");
+    REQUIRE(score_stride >= max_n, IDX_EINVAL, "idx_topk_pool: score_stride=%lld < max_n=%lld",
+            (long long)score_stride, (long long)max_n);
+    REQUIRE(pool_stride >= max_blocks, IDX_EINVAL, "idx_topk_pool: pool_stride=%lld < max_blocks=%d",
+            (long long)pool_stride, max_blocks);
+    REQUIRE(out_stride >= k, IDX_EINVAL, "idx_topk_pool: out_stride < k");
+    REQUIRE(aligned(scores, 4) && aligned(n_vis, 4) && aligned(pool_blocks, 4) && aligned(pool_count, 4) &&
+                aligned(out_idx, 4) && (!out_val || aligned(out_val, 4)),
+            IDX_EALIGN, "idx_topk_pool: pointers must be 4-byte aligned");
+    SelectArgs a{};
+    a.vals = scores;
+    a.stride = score_stride;
+    a.nv = n_vis;
+    a.nq = nq;
+    a.max_n = max_n;
+    a.k = k;
+    a.pool_mode = false;
+    a.map = pool_blocks;
+    a.map_stride = pool_stride;
+    a.map_values = true;
+    a.map_count = pool_count;
+    a.map_group = group;
+    a.map_width = max_blocks;
+    a.out_idx = out_idx;
+    a.out_stride = out_stride;
+    a.out_val = out_val;
+    a.out_count = nullptr;
+    a.pad_to = k;
+    a.ws = nullptr;
+    return hip_status(launch_select(a, (hipStream_t)stream), "idx_topk_pool");
+}
 
 idx_status idx_quantize_kv(const uint16_t* x_bf16, int64_t rows, uint8_t* codes, uint8_t* scales, void* stream) {
     REQUIRE(rows >= 0 && rows <= (int64_t)1 << 31, IDX_EINVAL, "idx_quantize_kv: rows=%lld out of [0, 2^31]",

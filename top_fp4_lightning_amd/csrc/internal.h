@@ -79,6 +79,14 @@ struct SelectArgs {
     // optional slot -> position map (top-k over pool-order scores)
     const int32_t* map;
     int64_t map_stride;
+    // map_values: the map indexes a full score row instead. Row t then holds
+    // 8 * min(map_count[t / map_group], map_width) slots, slot s is the value at position
+    // p = map[t / map_group][s / 8] * 8 + s % 8 of vals row t, and -inf where p >= n_t or the
+    // block id lies outside [0, ceil(n_t / 8))
+    bool map_values;
+    const int32_t* map_count;
+    int32_t map_group;
+    int64_t map_width;
     // outputs
     int32_t* out_idx;
     int64_t out_stride;

@@ -16,6 +16,9 @@
 //  - longer rows (candidate pool over 2^17 block maxima, full score rows): three launches over
 //    chunks of 4096 values (bound, collect, finish; ordered by kernel boundaries, no cross-block
 //    fences or waits); the finishing block orders the winners by position.
+// A row may also be read through a pool's block list from a full score row (map_values): slot
+// 8i + r holds the value at position 8 * block_i + r, so the top-k restricted to the pooled
+// blocks needs neither a masked copy of the row nor the long-row launches.
 #include "internal.h"
 
 namespace fp4idx {
@@ -48,19 +51,27 @@ __device__ __forceinline__ uint32_t comp_key(uint64_t c) { return (uint32_t)(c >
 __host__ __device__ inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 __host__ __device__ inline int64_t row_cap(const SelectArgs& a) {
+    if (a.map_values) return a.map_width * kBlock;
     return a.pool_mode ? (a.max_n + kBlock - 1) / kBlock : a.max_n;
 }
 
 struct RowInfo {
     int64_t len;  // values in this row
     int64_t pin;  // pinned element (pool mode) or -1
+    int64_t n;    // visible positions of the score row (map_values)
 };
 
 __device__ __forceinline__ RowInfo row_info(const SelectArgs& a, int64_t t) {
     int64_t n = a.nv ? (int64_t)a.nv[t] : a.max_n;
     n = n < 0 ? 0 : (n > a.max_n ? a.max_n : n);
     RowInfo ri;
-    if (a.pool_mode) {
+    ri.n = n;
+    if (a.map_values) {
+        int64_t c = a.map_count[t / a.map_group];
+        c = c < 0 ? 0 : (c > a.map_width ? a.map_width : c);
+        ri.len = c * kBlock;
+        ri.pin = -1;
+    } else if (a.pool_mode) {
         ri.len = (n + kBlock - 1) / kBlock;
         ri.pin = n > 0 ? (n - 1) / kBlock : -1;
     } else {
@@ -351,26 +362,56 @@ __device__ __forceinline__ uint64_t entry_composite(uint64_t x) {
     return ((uint64_t)order_key(__uint_as_float((uint32_t)(x >> 32))) << 32) | (x & 0xffffffffull);
 }
 
+// the 8 values of a run at byte offset off; values past the descriptor's range read as 0 (two
+// 16-byte loads per run measured no faster than these eight dword loads)
+__device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t rv, uint32_t off, float (&v)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, (int)(off + 4u * e), 0, 0));
+}
+
 template <int NT>
 __device__ __forceinline__ void chunk_load(const SelectArgs& a, int64_t t, const RowInfo& ri, int64_t c0,
                                            float (&v)[kRuns][8], uint32_t (&pb)[kRuns]) {
     const int64_t rem64 = ri.len - c0;
     const int rem = rem64 < (int64_t)(kRunSlots * NT) ? (int)rem64 : kRunSlots * NT;
     const int tid = threadIdx.x;
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(a.vals + t * a.stride + c0), 0, rem * 4, kSelRsrcWord3);
+    if (a.map_values) {
+        // block ids, then the 8 values of each block from the score row; ids outside the row's
+        // blocks and positions past n_t read as -inf (the loads are issued unconditionally, range
+        // checked by the descriptors, and the invalid ones replaced afterwards)
+        const int32_t* mrow = a.map + (t / a.map_group) * a.map_stride + c0 / kBlock;
+        const __amdgpu_buffer_rsrc_t rm =
+            __builtin_amdgcn_make_buffer_rsrc((void*)mrow, 0, ((rem + kBlock - 1) / kBlock) * 4, kSelRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.vals + t * a.stride), 0, (int)(ri.n * 4), kSelRsrcWord3);
+        const uint32_t nb = (uint32_t)((ri.n + kBlock - 1) / kBlock), n = (uint32_t)ri.n;
+        bool okb[kRuns];
 #pragma unroll
-    for (int r = 0; r < kRuns; ++r)
+        for (int r = 0; r < kRuns; ++r) {
+            const uint32_t id = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rm, (tid + r * NT) * 4, 0, 0);
+            okb[r] = id < nb;
+            pb[r] = okb[r] ? id * (uint32_t)kBlock : 0u;
+        }
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            v[r][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, (8 * (tid + r * NT) + e) * 4, 0, 0));
-    if (a.map) {
+        for (int r = 0; r < kRuns; ++r) load_run(rv, pb[r] * 4u, v[r]);
+#pragma unroll
+        for (int r = 0; r < kRuns; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (!(okb[r] && pb[r] + (uint32_t)e < n)) v[r][e] = -INFINITY;
+    } else {
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.vals + t * a.stride + c0), 0, rem * 4, kSelRsrcWord3);
+#pragma unroll
+        for (int r = 0; r < kRuns; ++r) load_run(rv, (uint32_t)(8 * (tid + r * NT)) * 4u, v[r]);
+    }
+    if (a.map && !a.map_values) {
         const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.map + t * a.map_stride + c0 / kBlock), 0, ((rem + kBlock - 1) / kBlock) * 4, kSelRsrcWord3);
 #pragma unroll
         for (int r = 0; r < kRuns; ++r)
             pb[r] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rm, (tid + r * NT) * 4, 0, 0) * (uint32_t)kBlock;
-    } else {
+    } else if (!a.map_values) {
 #pragma unroll
         for (int r = 0; r < kRuns; ++r) pb[r] = (uint32_t)(c0 + 8 * (tid + r * NT));
     }

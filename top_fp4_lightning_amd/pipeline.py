@@ -19,7 +19,8 @@ Training form ("DeepSeek-V4.1 model structure (3)", sections "three details of t
 code" and "the pool also acts in training"): every layer scores every visible position, and a
 Reindex layer sets the scores outside the pool to -inf before its top-512. MaskFormPlan runs it for
 all layers at once (the queries of every layer present together): one scan of the key cache
-serves every layer's query, then the pool, the mask and one top-512 per row.
+serves every layer's query, then the pool and one top-512 per row over the pooled positions
+(idx_topk_pool; or the literal in-place mask and a top-512 over whole rows).
 
 Prefill (a chunk of queries sharing one key range, causal): idx_score_full writes block maxima
 for every query; idx_topk keeps the 512 best blocks per query (a top-512 key's block is among
@@ -36,7 +37,7 @@ import numpy as np
 import torch
 
 from . import (BLOCK, IDX_OP_BUILD_POOL, IDX_OP_TOPK, idx_build_pool, idx_mask_pool, idx_quantize_q,
-               idx_score_full, idx_score_pool_gather, idx_topk, workspace)
+               idx_score_full, idx_score_pool_gather, idx_topk, idx_topk_pool, workspace)
 
 
 @dataclass
@@ -181,12 +182,18 @@ class MaskFormPlan:
     maxima the Full layer's pool is built from). The mask then applies each query's pool to all
     of its rows. On the Full layer's row it changes no top-512 entry: a key outside the pool is
     outranked by a key of each of the 2047 unpinned pooled blocks (their maxima beat or tie-win
-    its block's), so it never makes the top-512. The results equal DecodePlan's gather form."""
+    its block's), so it never makes the top-512. The results equal DecodePlan's gather form.
 
-    def __init__(self, dev: DeviceWorkload, k: int = 512, topk_blocks: int = 2048):
+    By default the mask and the top-512 are one call, idx_topk_pool, which reads each row only at
+    its query's pooled positions and leaves the scores unmasked. write_mask=True runs the literal
+    form instead: idx_mask_pool writes -inf outside the pool in place, then idx_topk selects over
+    whole rows (for callers that consume the masked scores)."""
+
+    def __init__(self, dev: DeviceWorkload, k: int = 512, topk_blocks: int = 2048, write_mask: bool = False):
         nq, max_n = dev.nq, dev.max_n
         d = dev.k_codes.device
-        self.dev, self.k, self.topk_blocks = dev, k, topk_blocks
+        self.dev, self.k, self.topk_blocks, self.write_mask = dev, k, topk_blocks, write_mask
+        self.max_blocks = min(topk_blocks, (max_n + BLOCK - 1) // BLOCK)
         self.L = L = len(dev.q)
         self.rows = rows = nq * L
         nb = (max_n + BLOCK - 1) // BLOCK
@@ -203,7 +210,7 @@ class MaskFormPlan:
         self.topk = torch.empty(rows, k, dtype=torch.int32, device=d)
         self.topk_val = torch.empty(rows, k, dtype=torch.float32, device=d)
         self.ws_pool = workspace(IDX_OP_BUILD_POOL, nq, max_n, topk_blocks, device=d)
-        self.ws_topk = workspace(IDX_OP_TOPK, rows, max(max_n, 1), k, device=d)
+        self.ws_topk = workspace(IDX_OP_TOPK, rows, max(max_n, 1), k, device=d) if write_mask else None
 
     def layer_topk(self, layer: int):
         """(indices, values) [nq, k] of one layer."""
@@ -221,9 +228,14 @@ class MaskFormPlan:
         full_bm = self.block_max.view(dv.nq, L, -1)[:, 0]  # the Full layer's rows
         idx_build_pool(full_bm, dv.n_vis, dv.max_n, self.pool_blocks, self.pool_count, self.ws_pool,
                        topk_blocks=self.topk_blocks, stream=stream)
-        idx_mask_pool(self.scores, self.n_vis, dv.max_n, self.pool_blocks, self.pool_count, group=L, stream=stream)
-        idx_topk(self.scores, dv.max_n, self.k, self.topk, self.ws_topk, n_valid=self.n_vis, out_val=self.topk_val,
-                 stream=stream)
+        if self.write_mask:
+            idx_mask_pool(self.scores, self.n_vis, dv.max_n, self.pool_blocks, self.pool_count, group=L,
+                          stream=stream)
+            idx_topk(self.scores, dv.max_n, self.k, self.topk, self.ws_topk, n_valid=self.n_vis,
+                     out_val=self.topk_val, stream=stream)
+        else:
+            idx_topk_pool(self.scores, self.n_vis, dv.max_n, self.pool_blocks, self.pool_count, self.max_blocks,
+                          self.k, self.topk, out_val=self.topk_val, group=L, stream=stream)
         return self
 
 
