@@ -130,7 +130,11 @@ def make_rows(rng, nq, n, kind):
                                       (8193, 512, "ties"), (4096, 2048, "equal"), (4000, 512, "ties"),
                                       # long rows whose bound admits every value (k large for the row),
                                       # so the candidates exceed what the finishing block stages in LDS
-                                      (20000, 2048, "normal"), (33000, 2048, "neginf"), (16385, 1, "ties")])
+                                      (20000, 2048, "normal"), (33000, 2048, "neginf"), (16385, 1, "ties"),
+                                      # k above 64 per wavefront: the bound from the lanes' second-largest
+                                      # values, candidates beyond the smaller list
+                                      (16384, 2048, "normal"), (12000, 2048, "ties"), (16384, 1500, "neginf"),
+                                      (16384, 1025, "equal")])
 def test_topk_exact(fx, n, k, kind):
     rng = np.random.default_rng(n + k)
     nq = 3
@@ -187,7 +191,8 @@ def adversarial_rows(rng, nq, n, kind, k):
 
 
 @pytest.mark.parametrize("kind", ["posinf_few", "posinf_many", "nan", "signed_zeros", "narrow", "sparse", "one_hot"])
-@pytest.mark.parametrize("n,k", [(16384, 512), (5000, 1025), (3000, 1), (70000, 512), (200000, 2048), (40000, 64)])
+@pytest.mark.parametrize("n,k", [(16384, 512), (5000, 1025), (3000, 1), (70000, 512), (200000, 2048), (40000, 64),
+                                 (16384, 2048)])
 def test_topk_adversarial(fx, n, k, kind):
     rng = np.random.default_rng(zlib.crc32(f"{n},{k},{kind}".encode()))
     nq = 2

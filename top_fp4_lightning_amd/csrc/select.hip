@@ -437,6 +437,22 @@ __device__ __forceinline__ void chunk_load(const SelectArgs& a, int64_t t, const
     }
 }
 
+// key of the thread's second-largest eligible value (a tie counts twice); 0 when the thread holds
+// fewer than two eligible values. Keys, not floats, so that -inf and NaN are never counted.
+__device__ __forceinline__ uint32_t lane_second(const float (&v)[kRuns][8]) {
+    uint32_t m1 = 0u, m2 = 0u;
+#pragma unroll
+    for (int r = 0; r < kRuns; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t k = order_key(v[r][e]);
+            const uint32_t x = eligible(k) ? k : 0u;
+            m2 = max(m2, min(m1, x));
+            m1 = max(m1, x);
+        }
+    return m2;
+}
+
 // key of the thread's largest value; 0 when the thread holds no eligible value
 __device__ __forceinline__ uint32_t lane_max(const float (&v)[kRuns][8]) {
     float fm = v[0][0];
@@ -611,12 +627,15 @@ __device__ uint64_t list_radix(const uint64_t* L, uint32_t C, uint32_t k, uint32
 }
 
 // ---------------------------------------------------------------- rows of <= 16 * NT values
-// One block per row, all four steps in registers and LDS. When R > 64 would be needed or the
+// One block per row, all four steps in registers and LDS. When R > 128 would be needed or the
 // candidates overflow the list, the radix passes run over the registers instead (wave-private
 // histograms) and the winners are compacted from the registers.
-template <int NT>
+template <int NT, bool WIDE>
 struct SmallShared {
-    static constexpr int kCap = 4 * NT;
+    // candidate list capacity. WIDE (launched when k needs more than 64 values per wavefront)
+    // keeps three times as many entries, enough for the looser bound of k = 2048 on a full row;
+    // the narrow list keeps the output step short for the usual k
+    static constexpr int kCap = (WIDE ? 12 : 4) * NT;
     union {
         Hist<NT> H;  // register passes
         struct {
@@ -630,11 +649,11 @@ struct SmallShared {
     Sel sel;
 };
 
-template <int NT>
+template <int NT, bool WIDE>
 __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
     constexpr int NW = NT / 64;
-    constexpr int kCap = SmallShared<NT>::kCap;
-    __shared__ SmallShared<NT> S;
+    constexpr int kCap = SmallShared<NT, WIDE>::kCap;
+    __shared__ SmallShared<NT, WIDE> S;
     const int64_t t = blockIdx.x;
     const RowInfo ri = row_info(a, t);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -642,9 +661,13 @@ __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
     uint32_t pb[kRuns];
     chunk_load<NT>(a, t, ri, 0, v, pb);
 
-    // 1. T0 (every wavefront must contribute here)
+    // 1. T0 (every wavefront must contribute here). Each wavefront needs R values at or above
+    // its contribution: the R-th largest of its lanes' maxima, or in the wide form for
+    // 64 < R <= 128 the ceil(R / 2)-th largest of its lanes' second-largest values (two values
+    // per such lane).
     const uint32_t R = ((uint32_t)a.k + NW - 1) / NW;
-    const uint32_t t0w = R <= 64 ? wave_rth(lane_max(v), R) : 0u;
+    const uint32_t t0w = R <= 64 ? wave_rth(lane_max(v), R)
+                                 : (WIDE && R <= 128 ? wave_rth(lane_second(v), (R + 1) / 2) : 0u);
     if (lane == 0) S.wt0[w] = t0w;
     __syncthreads();
     uint32_t T0 = S.wt0[0];
@@ -1009,16 +1032,19 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
     if (a.nq <= 0) return hipSuccess;
     const int64_t cap = row_cap(a);
     if (cap <= kSmallRow) {
-        // the block holds 16 values per thread, and T0 needs k <= NT to bound the candidates
+        // the block holds 16 values per thread, and T0 needs k <= NT (k <= 2 NT with the lanes'
+        // second-largest values, in the wide 1024-thread form) to bound the candidates
         const dim3 grid((unsigned)a.nq);
         const int64_t per_thread = (cap + 8 * kRuns - 1) / (8 * kRuns);
         const int64_t nt = per_thread > a.k ? per_thread : a.k;
         if (nt <= 256)
-            hipLaunchKernelGGL(select_small_kernel<256>, grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((select_small_kernel<256, false>), grid, dim3(256), 0, stream, a);
         else if (nt <= 512)
-            hipLaunchKernelGGL(select_small_kernel<512>, grid, dim3(512), 0, stream, a);
+            hipLaunchKernelGGL((select_small_kernel<512, false>), grid, dim3(512), 0, stream, a);
+        else if (a.k <= 1024)
+            hipLaunchKernelGGL((select_small_kernel<1024, false>), grid, dim3(1024), 0, stream, a);
         else
-            hipLaunchKernelGGL(select_small_kernel<1024>, grid, dim3(1024), 0, stream, a);
+            hipLaunchKernelGGL((select_small_kernel<1024, true>), grid, dim3(1024), 0, stream, a);
         return hipGetLastError();
     }
     const WsView v = ws_view(a.ws, a.nq, cap);
