@@ -632,9 +632,9 @@ __device__ uint64_t list_radix(const uint64_t* L, uint32_t C, uint32_t k, uint32
 // histograms) and the winners are compacted from the registers.
 template <int NT, bool WIDE>
 struct SmallShared {
-    // candidate list capacity. WIDE (launched when k needs more than 64 values per wavefront)
-    // keeps three times as many entries, enough for the looser bound of k = 2048 on a full row;
-    // the narrow list keeps the output step short for the usual k
+    // candidate list capacity. WIDE (launched when k needs more than 64 values per wavefront and
+    // the row is longer than the narrow list) keeps three times as many entries, enough for the
+    // looser bound of k = 2048 on a full row; the narrow list keeps the output step short
     static constexpr int kCap = (WIDE ? 12 : 4) * NT;
     union {
         Hist<NT> H;  // register passes
@@ -1041,7 +1041,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
             hipLaunchKernelGGL((select_small_kernel<256, false>), grid, dim3(256), 0, stream, a);
         else if (nt <= 512)
             hipLaunchKernelGGL((select_small_kernel<512, false>), grid, dim3(512), 0, stream, a);
-        else if (a.k <= 1024)
+        else if (a.k <= 1024 || cap <= SmallShared<1024, false>::kCap)  // the narrow list holds such a row whole
             hipLaunchKernelGGL((select_small_kernel<1024, false>), grid, dim3(1024), 0, stream, a);
         else
             hipLaunchKernelGGL((select_small_kernel<1024, true>), grid, dim3(1024), 0, stream, a);
