@@ -437,20 +437,27 @@ __device__ __forceinline__ void chunk_load(const SelectArgs& a, int64_t t, const
     }
 }
 
-// key of the thread's second-largest eligible value (a tie counts twice); 0 when the thread holds
-// fewer than two eligible values. Keys, not floats, so that -inf and NaN are never counted.
-__device__ __forceinline__ uint32_t lane_second(const float (&v)[kRuns][8]) {
-    uint32_t m1 = 0u, m2 = 0u;
+// key of the thread's M-th largest eligible value (ties count separately); 0 when the thread holds
+// fewer than M eligible values. Keys, not floats, so that -inf and NaN are never counted.
+template <int M>
+__device__ __forceinline__ uint32_t lane_mth(const float (&v)[kRuns][8]) {
+    uint32_t m[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) m[i] = 0u;
 #pragma unroll
     for (int r = 0; r < kRuns; ++r)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint32_t k = order_key(v[r][e]);
-            const uint32_t x = eligible(k) ? k : 0u;
-            m2 = max(m2, min(m1, x));
-            m1 = max(m1, x);
+            uint32_t x = eligible(k) ? k : 0u;
+#pragma unroll
+            for (int i = 0; i < M; ++i) {  // insert x into the descending m[0..M)
+                const uint32_t hi = max(m[i], x);
+                x = min(m[i], x);
+                m[i] = hi;
+            }
         }
-    return m2;
+    return m[M - 1];
 }
 
 // key of the thread's largest value; 0 when the thread holds no eligible value
@@ -663,11 +670,11 @@ __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
 
     // 1. T0 (every wavefront must contribute here). Each wavefront needs R values at or above
     // its contribution: the R-th largest of its lanes' maxima, or in the wide form for
-    // 64 < R <= 128 the ceil(R / 2)-th largest of its lanes' second-largest values (two values
-    // per such lane).
+    // 64 < R <= 128 the ceil(R / 4)-th largest of its lanes' fourth-largest values (four values
+    // per such lane; a middle lane's fourth value bounds tighter than the lowest lane's second)
     const uint32_t R = ((uint32_t)a.k + NW - 1) / NW;
     const uint32_t t0w = R <= 64 ? wave_rth(lane_max(v), R)
-                                 : (WIDE && R <= 128 ? wave_rth(lane_second(v), (R + 1) / 2) : 0u);
+                                 : (WIDE && R <= 128 ? wave_rth(lane_mth<4>(v), (R + 3) / 4) : 0u);
     if (lane == 0) S.wt0[w] = t0w;
     __syncthreads();
     uint32_t T0 = S.wt0[0];
@@ -1033,7 +1040,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
     const int64_t cap = row_cap(a);
     if (cap <= kSmallRow) {
         // the block holds 16 values per thread, and T0 needs k <= NT (k <= 2 NT with the lanes'
-        // second-largest values, in the wide 1024-thread form) to bound the candidates
+        // fourth-largest values, in the wide 1024-thread form) to bound the candidates
         const dim3 grid((unsigned)a.nq);
         const int64_t per_thread = (cap + 8 * kRuns - 1) / (8 * kRuns);
         const int64_t nt = per_thread > a.k ? per_thread : a.k;
