@@ -362,8 +362,8 @@ __device__ __forceinline__ uint64_t entry_composite(uint64_t x) {
     return ((uint64_t)order_key(__uint_as_float((uint32_t)(x >> 32))) << 32) | (x & 0xffffffffull);
 }
 
-// the 8 values of a run at byte offset off; values past the descriptor's range read as 0 (two
-// 16-byte loads per run measured no faster than these eight dword loads)
+// the 8 values of a run at byte offset off; values past the descriptor's range read as 0 (the
+// compiler merges the eight dword loads into two 16-byte loads)
 __device__ __forceinline__ void load_run(__amdgpu_buffer_rsrc_t rv, uint32_t off, float (&v)[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, (int)(off + 4u * e), 0, 0));
