@@ -150,6 +150,23 @@ idx_status idx_build_pool(const float* block_max, int64_t bm_stride, const int32
                           int64_t pool_stride, int32_t* pool_count, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * idx_build_pool_noalloc: idx_build_pool for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments,
+ * semantics and results as idx_build_pool, without the workspace: the selection's scratch is a
+ * fixed 80 MiB array inside the library, one copy per GPU, held until the process ends. The call
+ * allocates and frees nothing. The scratch is enough for nq rows of ceil(max_n / 8) block maxima
+ * up to idx_workspace_size(IDX_OP_BUILD_POOL, nq, max_n, topk_blocks) <= 80 MiB (e.g. 76 rows at
+ * max_n = 2^20); larger requests return IDX_EUNSUPPORTED before any HIP call.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's contents: calls
+ * that may overlap on one GPU (different streams without ordering) race and give unspecified
+ * results. The first call on a device (and any call with more rows than every call before it on
+ * that device) also enqueues a small kernel that clears the per-row counters it is about to use.
+ */
+idx_status idx_build_pool_noalloc(const float* block_max, int64_t bm_stride, const int32_t* n_vis, int32_t nq,
+                                  int64_t max_n, int32_t topk_blocks, int32_t block, int32_t* pool_blocks,
+                                  int64_t pool_stride, int32_t* pool_count, void* stream);
+
+/*
  * idx_score_pool_gather: Reindex-layer scoring restricted to the candidate pool. Only the key
  * rows of the listed blocks are read and scored with the layer's own q and w ([P1] "use
  * shallow-layer scores to limit deep-layer scoring": Reindex layers score only pool positions,

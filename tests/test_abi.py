@@ -119,6 +119,29 @@ def test_build_pool_validation(fx):
     assert f(*bad) == fx.IDX_EALIGN
 
 
+def test_build_pool_noalloc_validation(fx):
+    """the allocation-free pool: same argument checks, and requests beyond its fixed scratch are
+    rejected before any HIP call (so before its device address is ever resolved)"""
+    f = lambda *a: call(fx, "idx_build_pool_noalloc", *a)
+    good = [FAKE, 1 << 17, FAKE, 8, 1 << 20, 2048, 8, FAKE, 2048, FAKE, None]
+    bad = list(good); bad[6] = 4
+    assert f(*bad)[0] == fx.IDX_EUNSUPPORTED
+    bad = list(good); bad[0] = None
+    assert f(*bad)[0] == fx.IDX_EINVAL
+    bad = list(good); bad[8] = 100
+    assert f(*bad)[0] == fx.IDX_EINVAL
+    bad = list(good); bad[9] = FAKE + 2
+    assert f(*bad)[0] == fx.IDX_EALIGN
+    # 64 rows of 2^20 positions fit in 80 MiB; 128 rows do not
+    assert fx.workspace_size(fx.IDX_OP_BUILD_POOL, 64, 1 << 20, 2048) <= 80 << 20
+    assert fx.workspace_size(fx.IDX_OP_BUILD_POOL, 128, 1 << 20, 2048) > 80 << 20
+    bad = list(good); bad[3] = 128
+    st, msg = f(*bad)
+    assert st == fx.IDX_EUNSUPPORTED and "scratch" in msg
+    bad = list(good); bad[3] = 0
+    assert f(*bad)[0] == fx.IDX_OK  # nothing to do
+
+
 def test_gather_and_topk_validation(fx):
     g = lambda *a: call(fx, "idx_score_pool_gather", *a)[0]
     good = [FAKE, FAKE, FAKE, FAKE, 2, FAKE, 2048, FAKE, 2048, 8, FAKE, FAKE, FAKE, FAKE, 16384, None, None]

@@ -32,19 +32,21 @@ lib.idx_workspace_size.restype = _sz
 lib.idx_quantize_q.argtypes = [_P, _i64, _P, _P, _P, _P]
 lib.idx_score_full.argtypes = [_P, _P, _P, _P, _i32, _i32, _i64, _P, _P, _P, _P, _i64, _P, _i64, _P, _P]
 lib.idx_build_pool.argtypes = [_P, _i64, _P, _i32, _i64, _i32, _i32, _P, _i64, _P, _P, _sz, _P]
+lib.idx_build_pool_noalloc.argtypes = [_P, _i64, _P, _i32, _i64, _i32, _i32, _P, _i64, _P, _P]
 lib.idx_score_pool_gather.argtypes = [_P, _P, _P, _P, _i32, _P, _i64, _P, _i32, _i32, _P, _P, _P, _P, _i64, _P, _P]
 lib.idx_topk.argtypes = [_P, _i64, _P, _i32, _i64, _i32, _P, _i64, _i32, _P, _i64, _P, _P, _sz, _P]
 lib.idx_quantize_kv.argtypes = [_P, _i64, _P, _P, _P]
 lib.idx_gather_kv.argtypes = [_P, _P, _P, _P, _i32, _P, _i64, _i32, _P, _P]
 lib.idx_mask_pool.argtypes = [_P, _i64, _P, _i32, _i64, _P, _i64, _P, _i32, _i32, _P]
 lib.idx_topk_pool.argtypes = [_P, _i64, _P, _i32, _i64, _P, _i64, _P, _i32, _i32, _i32, _i32, _P, _i64, _P, _P]
-for _f in ("idx_quantize_q", "idx_score_full", "idx_build_pool", "idx_score_pool_gather", "idx_topk",
+for _f in ("idx_quantize_q", "idx_score_full", "idx_build_pool", "idx_build_pool_noalloc", "idx_score_pool_gather",
+           "idx_topk",
            "idx_quantize_kv", "idx_gather_kv", "idx_mask_pool", "idx_topk_pool"):
     getattr(lib, _f).restype = _i32
 
 EXPORTS = ("idx_abi_version", "idx_last_error", "idx_workspace_size", "idx_quantize_q", "idx_score_full",
-           "idx_build_pool", "idx_score_pool_gather", "idx_topk", "idx_quantize_kv", "idx_gather_kv",
-           "idx_mask_pool", "idx_topk_pool")
+           "idx_build_pool", "idx_build_pool_noalloc", "idx_score_pool_gather", "idx_topk", "idx_quantize_kv",
+           "idx_gather_kv", "idx_mask_pool", "idx_topk_pool")
 MKV_DIM = 512
 
 
@@ -146,6 +148,18 @@ def idx_build_pool(block_max, n_vis, max_n: int, pool_blocks, pool_count, ws, to
     _check(lib.idx_build_pool(_rows_ptr(block_max), block_max.stride(0), _ptr(n_vis), nq, max_n, topk_blocks, block,
                               _ptr(pool_blocks), pool_blocks.stride(0), _ptr(pool_count), _ptr(ws), ws.numel(),
                               _stream(stream)))
+    return pool_blocks, pool_count
+
+
+def idx_build_pool_noalloc(block_max, n_vis, max_n: int, pool_blocks, pool_count, topk_blocks: int = 2048,
+                           block: int = BLOCK, stream=None):
+    """idx_build_pool without a workspace (the library's fixed per-GPU scratch); allocates nothing."""
+    nq = n_vis.shape[0]
+    _need(block_max, torch.float32, "block_max")
+    _need(pool_blocks, torch.int32, "pool_blocks")
+    _check(lib.idx_build_pool_noalloc(_rows_ptr(block_max), block_max.stride(0), _ptr(n_vis), nq, max_n, topk_blocks,
+                                      block, _ptr(pool_blocks), pool_blocks.stride(0), _ptr(pool_count),
+                                      _stream(stream)))
     return pool_blocks, pool_count
 
 

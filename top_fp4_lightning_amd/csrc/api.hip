@@ -2,12 +2,22 @@
 // Every check runs before the first HIP call, so argument errors never touch the device.
 #include <stdarg.h>
 #include <stdio.h>
+#include <mutex>
 #include <string>
 
 #include "../../include/fp4idx.h"
 #include "internal.h"
 
 using namespace fp4idx;
+
+// ---- scratch of idx_build_pool_noalloc, for callers that cannot allocate ----
+// The selection workspace lives in this file-scope device array: one copy on every GPU the
+// library runs on, held until the process ends, shared by every call on that GPU (calls that
+// overlap on one GPU race). On the host, `scratch` is only a stand-in for the device symbol and is
+// never passed to a kernel or a copy: its device address is resolved once per device with
+// hipGetSymbolAddress and kept in g_scratch.
+constexpr size_t kScratchBytes = (size_t)80 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -50,6 +60,84 @@ size_t ws_bytes_for(int32_t op, int32_t nq, int64_t max_n, int32_t k) {
     if (op == IDX_OP_BUILD_POOL) return select_workspace_bytes(nq, (max_n + kBlock - 1) / kBlock, k);
     if (op == IDX_OP_TOPK) return select_workspace_bytes(nq, max_n, k);
     return 0;
+}
+
+
+// Validation shared by the two pool entry points; fills the selection arguments (all but the
+// workspace).
+idx_status pool_args(const char* fn, const float* block_max, int64_t bm_stride, const int32_t* n_vis, int32_t nq,
+                     int64_t max_n, int32_t topk_blocks, int32_t block, int32_t* pool_blocks, int64_t pool_stride,
+                     int32_t* pool_count, SelectArgs& a) {
+    REQUIRE(block == kBlock, IDX_EUNSUPPORTED, "%s: block=%d (only 8 is implemented)", fn, block);
+    REQUIRE(topk_blocks >= 1 && topk_blocks <= kMaxK, IDX_EUNSUPPORTED, "%s: topk_blocks=%d out of [1, 2048]", fn,
+            topk_blocks);
+    REQUIRE(nq >= 0 && nq <= kMaxQueries, IDX_EUNSUPPORTED, "%s: nq=%d out of [0, 65535]", fn, nq);
+    REQUIRE(max_n >= 0 && max_n <= kMaxN, IDX_EINVAL, "%s: max_n=%lld out of [0, 2^30]", fn, (long long)max_n);
+    if (nq == 0) return ok();
+    REQUIRE(block_max && n_vis && pool_blocks && pool_count, IDX_EINVAL, "%s: null pointer", fn);
+    REQUIRE(bm_stride >= (max_n + kBlock - 1) / kBlock, IDX_EINVAL, "%s: bm_stride < ceil(max_n/8)", fn);
+    REQUIRE(pool_stride >= topk_blocks, IDX_EINVAL, "%s: pool_stride=%lld < topk_blocks=%d", fn,
+            (long long)pool_stride, topk_blocks);
+    REQUIRE(aligned(block_max, 4) && aligned(n_vis, 4) && aligned(pool_blocks, 4) && aligned(pool_count, 4),
+            IDX_EALIGN, "%s: misaligned pointer", fn);
+    a.vals = block_max;
+    a.stride = bm_stride;
+    a.nv = n_vis;
+    a.nq = nq;
+    a.max_n = max_n;
+    a.k = topk_blocks;
+    a.pool_mode = true;
+    a.out_idx = pool_blocks;
+    a.out_stride = pool_stride;
+    a.out_count = pool_count;
+    a.pad_to = topk_blocks;
+    return ok();
+}
+
+
+constexpr int kMaxDevices = 64;
+struct DeviceScratch {
+    void* ptr;             // device address of this device's `scratch`
+    int32_t rows_cleared;  // per-row counters [0, rows_cleared) known to be zero
+};
+std::mutex g_scratch_mu;
+DeviceScratch g_scratch[kMaxDevices];
+
+__global__ void clear_bytes_kernel(uint8_t* p, size_t bytes) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < bytes; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+// This device's scratch address; on first use and whenever a call needs the counters of more rows
+// than any call before it, those counters are cleared on `stream` (a fill kernel, no memset) before
+// the call's own kernels. Every selection call restores the counters it uses to zero.
+idx_status device_scratch(int32_t nq, hipStream_t stream, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(IDX_EHIP, "idx_build_pool_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    REQUIRE(dev >= 0 && dev < kMaxDevices, IDX_EUNSUPPORTED, "idx_build_pool_noalloc: device %d above %d", dev,
+            kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    DeviceScratch& ds = g_scratch[dev];
+    if (!ds.ptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(IDX_EHIP, "idx_build_pool_noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        ds.ptr = p;
+        ds.rows_cleared = 0;
+    }
+    if (nq > ds.rows_cleared) {
+        const size_t from = select_counter_bytes(ds.rows_cleared), to = select_counter_bytes(nq);
+        const size_t bytes = to - from;
+        const unsigned blocks = (unsigned)((bytes + 255) / 256 < 1024 ? (bytes + 255) / 256 : 1024);
+        hipLaunchKernelGGL(clear_bytes_kernel, dim3(blocks), dim3(256), 0, stream, (uint8_t*)ds.ptr + from, bytes);
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(IDX_EHIP, "idx_build_pool_noalloc: clear: %s", hipGetErrorString(e));
+        ds.rows_cleared = nq;
+    }
+    *out = ds.ptr;
+    return ok();
 }
 
 }  // namespace
@@ -107,36 +195,34 @@ idx_status idx_score_full(const uint8_t* k_codes, const uint8_t* k_scales, const
 idx_status idx_build_pool(const float* block_max, int64_t bm_stride, const int32_t* n_vis, int32_t nq,
                           int64_t max_n, int32_t topk_blocks, int32_t block, int32_t* pool_blocks,
                           int64_t pool_stride, int32_t* pool_count, void* ws, size_t ws_bytes, void* stream) {
-    REQUIRE(block == kBlock, IDX_EUNSUPPORTED, "idx_build_pool: block=%d (only 8 is implemented)", block);
-    REQUIRE(topk_blocks >= 1 && topk_blocks <= kMaxK, IDX_EUNSUPPORTED, "idx_build_pool: topk_blocks=%d out of [1, 2048]",
-            topk_blocks);
-    REQUIRE(nq >= 0 && nq <= kMaxQueries, IDX_EUNSUPPORTED, "idx_build_pool: nq=%d out of [0, 65535]", nq);
-    REQUIRE(max_n >= 0 && max_n <= kMaxN, IDX_EINVAL, "idx_build_pool: max_n=%lld out of [0, 2^30]",
-            (long long)max_n);
-    if (nq == 0) return ok();
-    REQUIRE(block_max && n_vis && pool_blocks && pool_count, IDX_EINVAL, "idx_build_pool: null pointer");
-    REQUIRE(bm_stride >= (max_n + kBlock - 1) / kBlock, IDX_EINVAL, "idx_build_pool: bm_stride < ceil(max_n/8)");
-    REQUIRE(pool_stride >= topk_blocks, IDX_EINVAL, "idx_build_pool: pool_stride=%lld < topk_blocks=%d",
-            (long long)pool_stride, topk_blocks);
+    SelectArgs a{};
+    const idx_status st = pool_args("idx_build_pool", block_max, bm_stride, n_vis, nq, max_n, topk_blocks, block,
+                                    pool_blocks, pool_stride, pool_count, a);
+    if (st != IDX_OK || nq == 0) return st;
     const size_t need = ws_bytes_for(IDX_OP_BUILD_POOL, nq, max_n, topk_blocks);
     REQUIRE(ws && ws_bytes >= need, IDX_EWORKSPACE, "idx_build_pool: workspace %zu bytes, need %zu", ws_bytes, need);
-    REQUIRE(aligned(ws, 16) && aligned(block_max, 4) && aligned(n_vis, 4) && aligned(pool_blocks, 4) &&
-                aligned(pool_count, 4),
-            IDX_EALIGN, "idx_build_pool: misaligned pointer");
-    SelectArgs a{};
-    a.vals = block_max;
-    a.stride = bm_stride;
-    a.nv = n_vis;
-    a.nq = nq;
-    a.max_n = max_n;
-    a.k = topk_blocks;
-    a.pool_mode = true;
-    a.out_idx = pool_blocks;
-    a.out_stride = pool_stride;
-    a.out_count = pool_count;
-    a.pad_to = topk_blocks;
+    REQUIRE(aligned(ws, 16), IDX_EALIGN, "idx_build_pool: misaligned workspace");
     a.ws = ws;
     return hip_status(launch_select(a, (hipStream_t)stream), "idx_build_pool");
+}
+
+idx_status idx_build_pool_noalloc(const float* block_max, int64_t bm_stride, const int32_t* n_vis, int32_t nq,
+                                  int64_t max_n, int32_t topk_blocks, int32_t block, int32_t* pool_blocks,
+                                  int64_t pool_stride, int32_t* pool_count, void* stream) {
+    SelectArgs a{};
+    const idx_status st = pool_args("idx_build_pool_noalloc", block_max, bm_stride, n_vis, nq, max_n, topk_blocks,
+                                    block, pool_blocks, pool_stride, pool_count, a);
+    if (st != IDX_OK || nq == 0) return st;
+    const size_t need = ws_bytes_for(IDX_OP_BUILD_POOL, nq, max_n, topk_blocks);
+    REQUIRE(need <= kScratchBytes, IDX_EUNSUPPORTED,
+            "idx_build_pool_noalloc: nq=%d rows of max_n=%lld positions need %zu bytes of scratch, above the "
+            "library's fixed %zu",
+            nq, (long long)max_n, need, kScratchBytes);
+    void* ptr = nullptr;
+    const idx_status sst = device_scratch(nq, (hipStream_t)stream, &ptr);
+    if (sst != IDX_OK) return sst;
+    a.ws = ptr;
+    return hip_status(launch_select(a, (hipStream_t)stream), "idx_build_pool_noalloc");
 }
 
 idx_status idx_score_pool_gather(const uint8_t* k_codes, const uint8_t* k_scales, const int64_t* k_base,

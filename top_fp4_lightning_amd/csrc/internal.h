@@ -96,6 +96,9 @@ struct SelectArgs {
     void* ws;
 };
 size_t select_workspace_bytes(int32_t nq, int64_t max_n, int32_t k);
+// bytes at the start of a selection workspace that hold the per-row counters of rows 0 .. nq - 1
+// (zero before a call, restored to zero by it); the rest is written before it is read
+size_t select_counter_bytes(int32_t nq);
 
 // training form of the pool: -inf outside the pooled blocks, in place
 hipError_t launch_mask_pool(float* scores, int64_t score_stride, const int32_t* n_vis, int32_t nq, int64_t max_n,

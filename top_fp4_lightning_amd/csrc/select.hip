@@ -1035,6 +1035,8 @@ size_t select_workspace_bytes(int32_t nq, int64_t cap, int32_t k) {
            align_up((size_t)nq * (size_t)v.cap * 8);
 }
 
+size_t select_counter_bytes(int32_t nq) { return nq > 0 ? (size_t)nq * sizeof(RowState) : 0; }
+
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
     if (a.nq <= 0) return hipSuccess;
     const int64_t cap = row_cap(a);
