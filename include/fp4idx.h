@@ -94,7 +94,7 @@ idx_status idx_quantize_q(const uint16_t* x_bf16, int64_t rows, const int8_t* si
  *
  * ([P1] "Reindex layers score a million entries per token": the score equation with 32 heads of
  * 128 dims; [P3] Q&A: ReLU instead of softmax, query-generated weights), with q and k in MXFP4,
- * per-head dots computed exactly by scaled-FP4 matrix instructions and the head sum in fp32;
+ * per-head dots computed by scaled-FP4 matrix instructions and the head sum in fp32;
  * fused with the block maxima of the candidate pool, B_b = max_{8b <= s < 8b+8, s < n_t} I_{t,s}
  * with positions past n_t counting as -inf ([P1] "use shallow-layer scores to limit
  * deep-layer scoring" and the walk-through of the official pool code). The newest-block pin is
@@ -117,6 +117,19 @@ idx_status idx_quantize_q(const uint16_t* x_bf16, int64_t rows, const int8_t* si
  *   head_dots : device fp32 [nq][32][score_stride] or NULL: the per-head dots q_{t,j}.k_s
  *               (a debugging output; slow).
  * At least one of scores, block_max, head_dots must be non-NULL.
+ *
+ * Exactness precondition. For query head j and key s let the spread be the largest exponent sum
+ * (e_q[j][g] + e_k[s][g]) over the four groups g minus the smallest such sum among the groups whose
+ * 32 code products do not sum to zero. The matrix instruction aligns the four group sums to the
+ * largest group's exponent (also when that group sums to zero), so:
+ *  - spread <= 14: the dot is exact (hence the same fp32 value as the exact sum whenever that is
+ *    representable) and I is the fp32 head sum of exact terms, within 1e-5 * sum_j |w_j| ReLU(d_j)
+ *    of the exact score (measured on MI355X over random codes at every spread up to 40);
+ *  - spread > 14: low-order group sums may be dropped (entirely when the largest group cancels), so
+ *    dots, scores and block maxima are unspecified.
+ * Rows written by idx_quantize_q from activations have group exponents within a few units of each
+ * other (the rotation spreads a row's energy over all four groups); the seeded workloads of this
+ * library never exceed a spread of 9.
  */
 idx_status idx_score_full(const uint8_t* k_codes, const uint8_t* k_scales, const int64_t* k_base,
                           const int32_t* n_vis, int32_t nq, int32_t group, int64_t max_n, const uint8_t* q_codes,
@@ -174,7 +187,8 @@ idx_status idx_build_pool_noalloc(const float* block_max, int64_t bm_stride, con
  * needs a kernel that reads only pooled keys, after the mask-form reference code).
  *
  *   k_codes, k_scales, k_base, n_vis, q_codes, q_scales, w : as for idx_score_full (group 1);
- *                 n_vis values above 2^24 are clamped to 2^24.
+ *                 n_vis values above 2^24 are clamped to 2^24. The per-key arithmetic is the
+ *                 scan's, bit for bit, under the same exactness precondition (spread <= 14).
  *   blocks      : device int32 [nq][blocks_stride]; block ids (any order) of query t are
  *                 blocks[t][0 .. block_count[t] - 1].
  *   block_count : device int32 [nq]; values are clamped to [0, max_blocks].
