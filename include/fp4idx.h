@@ -180,6 +180,27 @@ idx_status idx_build_pool_noalloc(const float* block_max, int64_t bm_stride, con
                                   int64_t pool_stride, int32_t* pool_count, void* stream);
 
 /*
+ * idx_top_blocks: the k blocks of 8 positions with the largest block maxima, ranked by (value desc,
+ * block id asc) without any pin, for a layer's own top-k reached through its block maxima (a key
+ * among the top k outranks every other key of at most k - 1 blocks, so its block is among the top
+ * k blocks: [P1] "use shallow-layer scores to limit deep-layer scoring", the nesting argument of the
+ * pool). Used by chunked prefill: the top-512 blocks of each query, then idx_score_pool_gather over
+ * them and idx_topk with the block map. Row t holds ceil(n_t / 8) maxima; blocks whose maximum is
+ * -inf are never selected.
+ *
+ *   block_max, bm_stride, n_vis, max_n, block : as for idx_build_pool (n_vis counts positions).
+ *   k           : 1 .. 2048.
+ *   blocks      : device int32 [nq][blocks_stride], blocks_stride >= k: ascending block ids, -1 after
+ *                 count[t] (count[t] = min(k, blocks above -inf)).
+ *   count       : device int32 [nq] (written).
+ *   ws, ws_bytes: at least idx_workspace_size(IDX_OP_BUILD_POOL, nq, max_n, k) bytes, as for
+ *                 idx_build_pool.
+ */
+idx_status idx_top_blocks(const float* block_max, int64_t bm_stride, const int32_t* n_vis, int32_t nq, int64_t max_n,
+                          int32_t k, int32_t block, int32_t* blocks, int64_t blocks_stride, int32_t* count, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
  * idx_score_pool_gather: Reindex-layer scoring restricted to the candidate pool. Only the key
  * rows of the listed blocks are read and scored with the layer's own q and w ([P1] "use
  * shallow-layer scores to limit deep-layer scoring": Reindex layers score only pool positions,
@@ -222,7 +243,8 @@ idx_status idx_score_pool_gather(const uint8_t* k_codes, const uint8_t* k_scales
  *   blocks       : NULL, or a device int32 [nq][blocks_stride] block map as produced by
  *                  idx_build_pool: value slot s of row t stands for position
  *                  blocks[t][s / block] * block + s % block, and that position is both the
- *                  reported index and the tie-break key.
+ *                  reported index and the tie-break key. The ids of a row must be distinct (as
+ *                  idx_build_pool writes them); a repeated id gives an unspecified selection.
  *   block        : 8 when blocks is given (ignored otherwise).
  *   out_idx      : device int32 [nq][out_stride], out_stride >= k.
  *   out_val      : device fp32 [nq][out_stride] or NULL: the selected values in the same order
@@ -270,8 +292,9 @@ idx_status idx_mask_pool(float* scores, int64_t score_stride, const int32_t* n_v
  * candidates are the positions 8 * pool_blocks[p][i] + r (i < min(pool_count[p], max_blocks),
  * r < 8) below n_t; ids outside [0, ceil(n_t / 8)) contribute nothing. Ranking, ties and the -1 /
  * -inf padding are those of idx_topk; indices are absolute positions, in ascending order when
- * the block ids are ascending and distinct (as idx_build_pool writes them); a repeated id would
- * report its positions twice.
+ * the block ids are ascending (as idx_build_pool writes them). The block ids of a pool must be
+ * distinct: the ranking assumes that every position appears once, so a repeated id gives an
+ * unspecified selection.
  *
  *   scores       : device fp32 [nq][score_stride], score_stride >= max_n (read only).
  *   n_vis, max_n : device int32 [nq]; n_t = min(max(n_vis[t], 0), max_n); max_n 0 .. 2^28.

@@ -142,6 +142,24 @@ def test_build_pool_noalloc_validation(fx):
     assert f(*bad)[0] == fx.IDX_OK  # nothing to do
 
 
+def test_top_blocks_validation(fx):
+    ws = fx.workspace_size(fx.IDX_OP_BUILD_POOL, 4, 1 << 20, 512)
+    f = lambda *a: call(fx, "idx_top_blocks", *a)[0]
+    good = [FAKE, 1 << 17, FAKE, 4, 1 << 20, 512, 8, FAKE, 512, FAKE, FAKE, ws, None]
+    bad = list(good); bad[6] = 16
+    assert f(*bad) == fx.IDX_EUNSUPPORTED
+    bad = list(good); bad[5] = 0
+    assert f(*bad) == fx.IDX_EUNSUPPORTED
+    bad = list(good); bad[8] = 511
+    assert f(*bad) == fx.IDX_EINVAL
+    bad = list(good); bad[11] = ws - 1
+    assert f(*bad) == fx.IDX_EWORKSPACE
+    bad = list(good); bad[10] = None
+    assert f(*bad) == fx.IDX_EWORKSPACE
+    bad = list(good); bad[9] = FAKE + 1
+    assert f(*bad) == fx.IDX_EALIGN
+
+
 def test_gather_and_topk_validation(fx):
     g = lambda *a: call(fx, "idx_score_pool_gather", *a)[0]
     good = [FAKE, FAKE, FAKE, FAKE, 2, FAKE, 2048, FAKE, 2048, 8, FAKE, FAKE, FAKE, FAKE, 16384, None, None]

@@ -1,10 +1,13 @@
-"""Full-size GPU runs of every workload, checked against the oracle on sampled queries.
+"""Full-size GPU runs of every workload, checked against the oracle.
 
 The GPU path runs exactly as the benchmark runs it (DecodePlan / PrefillPlan over the whole
-batch). For a few sampled queries the oracle quantises that sequence's keys itself (from the
-seeded generator, never from GPU output) and scores every visible key exactly; the GPU's top-512,
-pool and Reindex selections of those queries must match it under the boundary tolerance.
-The oracle calls are spread over host threads (ctypes releases the GIL).
+batch). Every query is checked element by element on a seeded sample: the block maxima of about
+256 of its blocks (and of its last, ragged block) and, for decode, the gathered scores of 64 of
+its pooled slots in every layer, against the oracle's scores of those keys (quantised by the
+oracle from the seeded generator, never from GPU output). For a few sampled queries the oracle
+also scores every visible key; the GPU's top-512, pool and Reindex selections of those queries
+must match it under the boundary tolerance. The oracle calls are spread over host threads
+(ctypes releases the GIL).
 """
 from concurrent.futures import ThreadPoolExecutor
 import os
@@ -57,6 +60,107 @@ def oracle_scores(qc, qs, w, kc, ks):
     return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
 
 
+class KeyBlocks:
+    """bf16 key rows of whole 8-position blocks of one sequence, regenerated from the seeded
+    generator (the planted set and shift computed once per sequence)."""
+
+    def __init__(self, wl, b):
+        self.wl, self.b = wl, b
+        self.n = int(wl.seq_len[b])
+        self.pos = wl.planted(b)
+        self.shift = synth.plant_shift(wl.q(0, [int(wl.plant_query[b])])[0]) if len(self.pos) else None
+
+    def rows(self, start, cnt):
+        rows = synth.normal_bf16(self.wl.seed, synth.TAG_K, self.b, start * 128, cnt * 128).reshape(cnt, 128)
+        if self.shift is not None:
+            synth.lib().synth_apply_plant(rows.ctypes.data, start, cnt, self.pos.ctypes.data, len(self.pos),
+                                          self.shift.ctypes.data)
+        return rows
+
+
+def sample_blocks(rng, nb, count=256):
+    """about `count` distinct seeded block ids of a row of nb blocks, always with the last one"""
+    if nb <= 0:
+        return np.zeros(0, np.int64)
+    pick = rng.choice(nb, size=min(count, nb), replace=False)
+    return np.unique(np.concatenate([pick, [nb - 1]])).astype(np.int64)
+
+
+def check_sampled_block_maxima(wl, t, n, bm_gpu_row, kb: "KeyBlocks", qc, qs, w, rng, count=256, what=""):
+    """GPU block maxima of query t on sampled blocks, against the oracle's scores of their keys"""
+    nb = (n + 7) // 8
+    blocks = sample_blocks(rng, nb, count)
+    rows, owner = [], []
+    for blk in blocks:
+        s0 = 8 * int(blk)
+        cnt = min(8, n - s0)
+        rows.append(kb.rows(s0, cnt))
+        owner.extend([int(blk)] * cnt)
+    rows = np.concatenate(rows) if rows else np.zeros((0, 128), np.uint16)
+    kc, ks = oracle.quantize(rows, wl.signs(), nthreads=1)
+    I, A = oracle.score_rows(qc, qs, w, kc, ks)
+    owner = np.asarray(owner)
+    for blk in blocks:
+        m = owner == blk
+        ref, a = I[m].max(), A[m].max()
+        got = float(bm_gpu_row[blk])
+        assert abs(got - ref) <= 1e-5 * max(a, 1e-30), f"{what} q{t} block {blk}: {got!r} vs {ref!r}"
+    return len(blocks)
+
+
+def check_sampled_pool_scores(wl, t, n, layer, pool_row, cnt, scores_row, kb, signs, rng, count=64, what=""):
+    """gathered pool-order scores of one layer on sampled slots, against the oracle"""
+    slots = np.arange(8 * int(cnt))
+    if len(slots) == 0:
+        return 0
+    pick = np.sort(rng.choice(slots, size=min(count, len(slots)), replace=False))
+    pos = 8 * pool_row[pick // 8].astype(np.int64) + pick % 8
+    valid = pos < n
+    for s_, p_ in zip(pick[~valid], pos[~valid]):
+        assert np.isneginf(scores_row[s_]), f"{what} q{t} layer {layer} slot {s_} past n"
+    pick, pos = pick[valid], pos[valid]
+    if len(pos) == 0:
+        return 0
+    rows = np.concatenate([kb.rows(int(p_), 1) for p_ in pos])
+    kc, ks = oracle.quantize(rows, signs, nthreads=1)
+    qc, qs = oracle.quantize(wl.q(layer, [t])[0], signs)
+    I, A = oracle.score_rows(qc, qs, wl.w(layer, [t])[0], kc, ks)
+    got = scores_row[pick].astype(np.float64)
+    bad = np.abs(got - I) > 1e-5 * np.maximum(A, 1e-30)
+    assert not bad.any(), f"{what} q{t} layer {layer}: {int(bad.sum())} gathered scores out of tolerance"
+    return len(pos)
+
+
+def check_every_decode_query(wl, out, what):
+    """element-wise coverage of every query of a decode batch: sampled block maxima of the Full
+    scan and sampled gathered scores of every layer"""
+    plan = out["plan"]
+    signs = wl.signs()
+    bm_gpu = out["block_max"].cpu().numpy()
+    pbk, pcn = out["pool_blocks"].cpu().numpy(), out["pool_count"].cpu().numpy()
+    ps = [x.cpu().numpy() for x in plan.pool_scores]
+    seqs = {}
+
+    def one(t):
+        rng = np.random.default_rng(1000 + t)
+        b = int(wl.qseq[t])
+        n = int(wl.n_vis[t])
+        kb = seqs[b]
+        qc, qs = oracle.quantize(wl.q(0, [t])[0], signs)
+        nblk = check_sampled_block_maxima(wl, t, n, bm_gpu[t], kb, qc, qs, wl.w(0, [t])[0], rng, what=what)
+        nsl = 0
+        for layer in range(plan.layers + 1):
+            nsl += check_sampled_pool_scores(wl, t, n, layer, pbk[t], pcn[t], ps[layer][t], kb, signs, rng, what=what)
+        return nblk, nsl
+
+    for b in sorted(set(int(x) for x in wl.qseq)):
+        seqs[b] = KeyBlocks(wl, b)
+    with ThreadPoolExecutor(THREADS) as ex:
+        res = list(ex.map(one, range(wl.nq)))
+    print(f"{what}: every query checked: {sum(r[0] for r in res)} sampled block maxima, "
+          f"{sum(r[1] for r in res)} sampled gathered scores", flush=True)
+
+
 def check_decode_queries(wl, out, sample, k=512):
     s = wl.signs()
     top = out["topk"].cpu().numpy()
@@ -102,6 +206,7 @@ def test_fullscan_1m(pl):
     # 8 x 2^20 keys (decoder, m = 1) with 4 Reindex layers: the benchmark's workload
     wl = synth.config("fullscan_1m")
     out = run_decode(pl, wl)
+    check_every_decode_query(wl, out, "fullscan_1m")
     check_decode_queries(wl, out, sample=[0, 7])
 
 
@@ -129,6 +234,7 @@ def test_fullscan_512k(pl):
     # 8 x 2^19 keys (encoder shape, m = 2)
     wl = synth.config("fullscan_512k")
     out = run_decode(pl, wl)
+    check_every_decode_query(wl, out, "fullscan_512k")
     check_decode_queries(wl, out, sample=[3])
 
 
@@ -136,6 +242,7 @@ def test_decode_batch64(pl):
     # 64 sequences with lengths in [64K, 128K]
     wl = synth.config("decode_batch64")
     out = run_decode(pl, wl)
+    check_every_decode_query(wl, out, "decode_batch64")
     order = np.argsort(wl.n_vis)
     check_decode_queries(wl, out, sample=[int(order[0]), int(order[-1]), 17])
 
@@ -144,6 +251,7 @@ def test_reindex_1m(pl):
     # 64 x 2^20 keys, pool from the Full layer, 4 Reindex layers with their own q and w
     wl = synth.config("reindex_1m")
     out = run_decode(pl, wl)
+    check_every_decode_query(wl, out, "reindex_1m")
     check_decode_queries(wl, out, sample=[0, 63])
 
 
@@ -152,6 +260,7 @@ def test_spec_decode_1m(pl):
     # the many-query kernel; pool, Full top-512 and 4 Reindex layers per position
     wl = synth.config("spec_decode_1m")
     out = run_decode(pl, wl)
+    check_every_decode_query(wl, out, "spec_decode_1m")
     check_decode_queries(wl, out, sample=[0, 5, 46])
 
 
@@ -187,6 +296,28 @@ def test_prefill_128k(pl):
     top = plan.topk.cpu().numpy()
     s = wl.signs()
     kc, ks = oracle_keys(wl, 0, int(wl.seq_len[0]), s)
+    bm_gpu = plan.block_max.cpu().numpy()
+
+    def every(t):
+        # every query: its block maxima on ~256 seeded blocks (and its last, ragged one)
+        rng = np.random.default_rng(5000 + t)
+        n = int(wl.n_vis[t])
+        nb = (n + 7) // 8
+        blocks = sample_blocks(rng, nb, 256)
+        pos = (8 * blocks[:, None] + np.arange(8)[None, :]).reshape(-1)
+        pos = pos[pos < n]
+        qc, qs = oracle.quantize(wl.q(0, [t])[0], s)
+        I, A = oracle.score_rows(qc, qs, wl.w(0, [t])[0], kc[pos], ks[pos])
+        owner = pos // 8
+        for blk in blocks:
+            m = owner == blk
+            ref, a = I[m].max(), A[m].max()
+            assert abs(float(bm_gpu[t, blk]) - ref) <= 1e-5 * max(a, 1e-30), f"prefill q{t} block {blk}"
+        return len(blocks)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        nblk = sum(ex.map(every, range(wl.nq)))
+    print(f"prefill_128k: every query checked: {nblk} sampled block maxima", flush=True)
     for t in [0, 1, 1000, 2047, 4094, 4095]:
         n = int(wl.n_vis[t])
         qc, qs = oracle.quantize(wl.q(0, [t])[0], s)

@@ -131,7 +131,7 @@ def make_rows(rng, nq, n, kind):
                                       # long rows whose bound admits every value (k large for the row),
                                       # so the candidates exceed what the finishing block stages in LDS
                                       (20000, 2048, "normal"), (33000, 2048, "neginf"), (16385, 1, "ties"),
-                                      # k above 64 per wavefront: the bound from the lanes' second-largest
+                                      # k above 64 per wavefront: the bound from the lanes' fourth-largest
                                       # values, candidates beyond the smaller list
                                       (16384, 2048, "normal"), (12000, 2048, "ties"), (16384, 1500, "neginf"),
                                       (16384, 1025, "equal")])
@@ -260,6 +260,32 @@ def test_build_pool_exact(fx, n):
         assert pc[t] == len(ref)
         assert np.array_equal(pb[t, :len(ref)], ref)
         assert (pb[t, len(ref):] == -1).all()
+
+
+@pytest.mark.parametrize("n,k", [(1, 512), (9, 512), (4096 * 8, 512), (4097 * 8 + 3, 512), (131072 * 8 + 5, 512),
+                                 (300001, 2048), (1 << 20, 7)])
+def test_top_blocks_exact(fx, n, k):
+    """idx_top_blocks: the k largest raw block maxima (ties to the lower block id, no pin),
+    ascending ids and counts, against the oracle's full-sort top-k over the block maxima."""
+    rng = np.random.default_rng(n + k)
+    nq = 3
+    nb = (n + 7) // 8
+    bm = rng.standard_normal((nq, nb)).astype(np.float32)
+    bm[1] = np.round(bm[1])  # ties
+    bm[2, ::3] = -np.inf  # blocks that can never be selected
+    nv = np.array([n, n, n], np.int32)
+    ws = fx.workspace(fx.IDX_OP_BUILD_POOL, nq, n, k)
+    out = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((nq,), -7, dtype=torch.int32, device="cuda")
+    fx.idx_top_blocks(torch.from_numpy(bm).cuda(), torch.from_numpy(nv).cuda(), n, k, out, cnt, ws)
+    torch.cuda.synchronize()
+    out, cnt = out.cpu().numpy(), cnt.cpu().numpy()
+    for t in range(nq):
+        ref = oracle.topk(bm[t].astype(np.float64), k)
+        ref = np.sort(ref[ref >= 0])
+        assert cnt[t] == len(ref), (t, cnt[t], len(ref))
+        assert np.array_equal(out[t, :len(ref)], ref), t
+        assert (out[t, len(ref):] == -1).all()
 
 
 def test_gather_matches_full_scan(fx, pl):

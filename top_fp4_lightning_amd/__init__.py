@@ -33,19 +33,21 @@ lib.idx_quantize_q.argtypes = [_P, _i64, _P, _P, _P, _P]
 lib.idx_score_full.argtypes = [_P, _P, _P, _P, _i32, _i32, _i64, _P, _P, _P, _P, _i64, _P, _i64, _P, _P]
 lib.idx_build_pool.argtypes = [_P, _i64, _P, _i32, _i64, _i32, _i32, _P, _i64, _P, _P, _sz, _P]
 lib.idx_build_pool_noalloc.argtypes = [_P, _i64, _P, _i32, _i64, _i32, _i32, _P, _i64, _P, _P]
+lib.idx_top_blocks.argtypes = [_P, _i64, _P, _i32, _i64, _i32, _i32, _P, _i64, _P, _P, _sz, _P]
 lib.idx_score_pool_gather.argtypes = [_P, _P, _P, _P, _i32, _P, _i64, _P, _i32, _i32, _P, _P, _P, _P, _i64, _P, _P]
 lib.idx_topk.argtypes = [_P, _i64, _P, _i32, _i64, _i32, _P, _i64, _i32, _P, _i64, _P, _P, _sz, _P]
 lib.idx_quantize_kv.argtypes = [_P, _i64, _P, _P, _P]
 lib.idx_gather_kv.argtypes = [_P, _P, _P, _P, _i32, _P, _i64, _i32, _P, _P]
 lib.idx_mask_pool.argtypes = [_P, _i64, _P, _i32, _i64, _P, _i64, _P, _i32, _i32, _P]
 lib.idx_topk_pool.argtypes = [_P, _i64, _P, _i32, _i64, _P, _i64, _P, _i32, _i32, _i32, _i32, _P, _i64, _P, _P]
-for _f in ("idx_quantize_q", "idx_score_full", "idx_build_pool", "idx_build_pool_noalloc", "idx_score_pool_gather",
-           "idx_topk",
+for _f in ("idx_quantize_q", "idx_score_full", "idx_build_pool", "idx_build_pool_noalloc", "idx_top_blocks",
+           "idx_score_pool_gather", "idx_topk",
            "idx_quantize_kv", "idx_gather_kv", "idx_mask_pool", "idx_topk_pool"):
     getattr(lib, _f).restype = _i32
 
 EXPORTS = ("idx_abi_version", "idx_last_error", "idx_workspace_size", "idx_quantize_q", "idx_score_full",
-           "idx_build_pool", "idx_build_pool_noalloc", "idx_score_pool_gather", "idx_topk", "idx_quantize_kv",
+           "idx_build_pool", "idx_build_pool_noalloc", "idx_top_blocks", "idx_score_pool_gather", "idx_topk",
+           "idx_quantize_kv",
            "idx_gather_kv", "idx_mask_pool", "idx_topk_pool")
 MKV_DIM = 512
 
@@ -161,6 +163,16 @@ def idx_build_pool_noalloc(block_max, n_vis, max_n: int, pool_blocks, pool_count
                                       block, _ptr(pool_blocks), pool_blocks.stride(0), _ptr(pool_count),
                                       _stream(stream)))
     return pool_blocks, pool_count
+
+
+def idx_top_blocks(block_max, n_vis, max_n: int, k: int, blocks, count, ws, block: int = BLOCK, stream=None):
+    """Top-k blocks by raw block maxima (no pin): ascending ids [nq, >= k] and counts [nq]."""
+    nq = n_vis.shape[0]
+    _need(block_max, torch.float32, "block_max")
+    _need(blocks, torch.int32, "blocks")
+    _check(lib.idx_top_blocks(_rows_ptr(block_max), block_max.stride(0), _ptr(n_vis), nq, max_n, k, block,
+                              _rows_ptr(blocks), blocks.stride(0), _ptr(count), _ptr(ws), ws.numel(), _stream(stream)))
+    return blocks, count
 
 
 def idx_score_pool_gather(k_codes, k_scales, k_base, n_vis, blocks, block_count, max_blocks: int, q_codes,

@@ -67,7 +67,7 @@ size_t ws_bytes_for(int32_t op, int32_t nq, int64_t max_n, int32_t k) {
 // workspace).
 idx_status pool_args(const char* fn, const float* block_max, int64_t bm_stride, const int32_t* n_vis, int32_t nq,
                      int64_t max_n, int32_t topk_blocks, int32_t block, int32_t* pool_blocks, int64_t pool_stride,
-                     int32_t* pool_count, SelectArgs& a) {
+                     int32_t* pool_count, bool pin, SelectArgs& a) {
     REQUIRE(block == kBlock, IDX_EUNSUPPORTED, "%s: block=%d (only 8 is implemented)", fn, block);
     REQUIRE(topk_blocks >= 1 && topk_blocks <= kMaxK, IDX_EUNSUPPORTED, "%s: topk_blocks=%d out of [1, 2048]", fn,
             topk_blocks);
@@ -87,6 +87,7 @@ idx_status pool_args(const char* fn, const float* block_max, int64_t bm_stride, 
     a.max_n = max_n;
     a.k = topk_blocks;
     a.pool_mode = true;
+    a.pin = pin;
     a.out_idx = pool_blocks;
     a.out_stride = pool_stride;
     a.out_count = pool_count;
@@ -197,7 +198,7 @@ idx_status idx_build_pool(const float* block_max, int64_t bm_stride, const int32
                           int64_t pool_stride, int32_t* pool_count, void* ws, size_t ws_bytes, void* stream) {
     SelectArgs a{};
     const idx_status st = pool_args("idx_build_pool", block_max, bm_stride, n_vis, nq, max_n, topk_blocks, block,
-                                    pool_blocks, pool_stride, pool_count, a);
+                                    pool_blocks, pool_stride, pool_count, true, a);
     if (st != IDX_OK || nq == 0) return st;
     const size_t need = ws_bytes_for(IDX_OP_BUILD_POOL, nq, max_n, topk_blocks);
     REQUIRE(ws && ws_bytes >= need, IDX_EWORKSPACE, "idx_build_pool: workspace %zu bytes, need %zu", ws_bytes, need);
@@ -211,7 +212,7 @@ idx_status idx_build_pool_noalloc(const float* block_max, int64_t bm_stride, con
                                   int64_t pool_stride, int32_t* pool_count, void* stream) {
     SelectArgs a{};
     const idx_status st = pool_args("idx_build_pool_noalloc", block_max, bm_stride, n_vis, nq, max_n, topk_blocks,
-                                    block, pool_blocks, pool_stride, pool_count, a);
+                                    block, pool_blocks, pool_stride, pool_count, true, a);
     if (st != IDX_OK || nq == 0) return st;
     const size_t need = ws_bytes_for(IDX_OP_BUILD_POOL, nq, max_n, topk_blocks);
     REQUIRE(need <= kScratchBytes, IDX_EUNSUPPORTED,
@@ -223,6 +224,20 @@ idx_status idx_build_pool_noalloc(const float* block_max, int64_t bm_stride, con
     if (sst != IDX_OK) return sst;
     a.ws = ptr;
     return hip_status(launch_select(a, (hipStream_t)stream), "idx_build_pool_noalloc");
+}
+
+idx_status idx_top_blocks(const float* block_max, int64_t bm_stride, const int32_t* n_vis, int32_t nq, int64_t max_n,
+                          int32_t k, int32_t block, int32_t* blocks, int64_t blocks_stride, int32_t* count, void* ws,
+                          size_t ws_bytes, void* stream) {
+    SelectArgs a{};
+    const idx_status st = pool_args("idx_top_blocks", block_max, bm_stride, n_vis, nq, max_n, k, block, blocks,
+                                    blocks_stride, count, false, a);
+    if (st != IDX_OK || nq == 0) return st;
+    const size_t need = ws_bytes_for(IDX_OP_BUILD_POOL, nq, max_n, k);
+    REQUIRE(ws && ws_bytes >= need, IDX_EWORKSPACE, "idx_top_blocks: workspace %zu bytes, need %zu", ws_bytes, need);
+    REQUIRE(aligned(ws, 16), IDX_EALIGN, "idx_top_blocks: misaligned workspace");
+    a.ws = ws;
+    return hip_status(launch_select(a, (hipStream_t)stream), "idx_top_blocks");
 }
 
 idx_status idx_score_pool_gather(const uint8_t* k_codes, const uint8_t* k_scales, const int64_t* k_base,

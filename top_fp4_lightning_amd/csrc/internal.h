@@ -76,6 +76,7 @@ struct SelectArgs {
     // pool mode: vals are block maxima, nv are visible positions, the row holds ceil(n_t / 8)
     // values and the block of position n_t - 1 is pinned to +inf; output ascending block ids
     bool pool_mode;
+    bool pin;  // pool mode: pin the block of position n_t - 1 (the candidate pool); false ranks raw maxima
     // optional slot -> position map (top-k over pool-order scores)
     const int32_t* map;
     int64_t map_stride;

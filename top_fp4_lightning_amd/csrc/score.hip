@@ -277,14 +277,8 @@ constexpr int kScanIters = 1;
 // of a few short-lived waves), several steps when it is large (prefill: the query is loaded once
 // per wavefront and the next step's keys are in flight while the current step computes).
 constexpr int kGatherIters = 1;
-#ifndef FP4IDX_GATHER_ITERS_MANY
-#define FP4IDX_GATHER_ITERS_MANY 4
-#endif
-constexpr int kGatherItersMany = FP4IDX_GATHER_ITERS_MANY;
-#ifndef FP4IDX_GATHER_MANY_SLOTS
-#define FP4IDX_GATHER_MANY_SLOTS (1 << 22)
-#endif
-constexpr int64_t kGatherManySlots = FP4IDX_GATHER_MANY_SLOTS;  // slots per launch from which the long form runs
+constexpr int kGatherItersMany = 4;
+constexpr int64_t kGatherManySlots = (int64_t)1 << 22;  // slots per launch from which the long form runs
 }  // namespace
 
 hipError_t launch_score_full(const ScoreArgs& a, hipStream_t stream) {

@@ -99,10 +99,7 @@ __device__ __forceinline__ float combine2(float p0, float p1) {
 constexpr int kStepKeys = 64;
 constexpr int kStageSteps = 2;                      // 64-key steps per staged block (one barrier)
 constexpr int kStageCodes = kStepKeys * kRowBytes;  // bytes of codes per step
-#ifndef FP4IDX_MULTI_BUFS
-#define FP4IDX_MULTI_BUFS 3
-#endif
-constexpr int kBufs = FP4IDX_MULTI_BUFS;  // staged blocks in LDS: kBufs - 1 in flight while one is scored
+constexpr int kBufs = 3;  // staged blocks in LDS: kBufs - 1 in flight while one is scored
 
 struct StageBuf {
     alignas(16) uint8_t codes[kBufs][kStageSteps][kStageCodes];
@@ -283,16 +280,10 @@ __global__ __launch_bounds__(256) void score_multi_kernel(ScoreArgs a) {
     }
 }
 
-#ifndef FP4IDX_MULTI_QW
-#define FP4IDX_MULTI_QW 2
-#endif
-#ifndef FP4IDX_MULTI_KT
-#define FP4IDX_MULTI_KT 32
-#endif
 // queries per wave in the many-query scan: two keep a wave within 128 registers, i.e. four
 // waves per SIMD, which hide the matrix-result latency of each other
-constexpr int kMultiQ = FP4IDX_MULTI_QW;
-constexpr int kMultiIters = FP4IDX_MULTI_KT;  // 64-key steps per block (2048 keys)
+constexpr int kMultiQ = 2;
+constexpr int kMultiIters = 32;  // 64-key steps per block (2048 keys)
 
 }  // namespace
 

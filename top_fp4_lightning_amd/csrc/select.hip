@@ -73,7 +73,7 @@ __device__ __forceinline__ RowInfo row_info(const SelectArgs& a, int64_t t) {
         ri.pin = -1;
     } else if (a.pool_mode) {
         ri.len = (n + kBlock - 1) / kBlock;
-        ri.pin = n > 0 ? (n - 1) / kBlock : -1;
+        ri.pin = (a.pin && n > 0) ? (n - 1) / kBlock : -1;
     } else {
         ri.len = n;
         ri.pin = -1;

@@ -23,7 +23,7 @@ serves every layer's query, then the pool and one top-512 per row over the poole
 (idx_topk_pool; or the literal in-place mask and a top-512 over whole rows).
 
 Prefill (a chunk of queries sharing one key range, causal): idx_score_full writes block maxima
-for every query; idx_topk keeps the 512 best blocks per query (a top-512 key's block is among
+for every query; idx_top_blocks keeps the 512 best blocks per query (a top-512 key's block is among
 them); idx_score_pool_gather re-scores those 4096 keys; idx_topk takes the final 512.
 
 All buffers are allocated once in the plan objects, so a step allocates nothing and can be
@@ -37,7 +37,7 @@ import numpy as np
 import torch
 
 from . import (BLOCK, IDX_OP_BUILD_POOL, IDX_OP_TOPK, idx_build_pool, idx_mask_pool, idx_quantize_q,
-               idx_score_full, idx_score_pool_gather, idx_topk, idx_topk_pool, workspace)
+               idx_score_full, idx_score_pool_gather, idx_top_blocks, idx_topk, idx_topk_pool, workspace)
 
 
 @dataclass
@@ -251,14 +251,13 @@ class PrefillPlan:
         self.q_codes = torch.empty(nq, 32, 64, dtype=torch.uint8, device=d)
         self.q_scales = torch.empty(nq, 32, 4, dtype=torch.uint8, device=d)
         self.block_max = torch.empty(nq, max(nb, 1), dtype=torch.float32, device=d)
-        self.n_blocks = ((dev.n_vis.to(torch.int64) + BLOCK - 1) // BLOCK).to(torch.int32)
         self.kb = min(k, nb)
         self.top_blocks = torch.empty(nq, k, dtype=torch.int32, device=d)
-        self.block_count = torch.full((nq,), self.kb, dtype=torch.int32, device=d)
+        self.block_count = torch.empty(nq, dtype=torch.int32, device=d)
         self.cand_scores = torch.empty(nq, max(self.kb * BLOCK, 1), dtype=torch.float32, device=d)
         self.topk = torch.empty(nq, k, dtype=torch.int32, device=d)
         self.topk_val = torch.empty(nq, k, dtype=torch.float32, device=d)
-        self.ws_blocks = workspace(IDX_OP_TOPK, nq, max(nb, 1), k, device=d)
+        self.ws_blocks = workspace(IDX_OP_BUILD_POOL, nq, max(max_n, 1), k, device=d)
         self.ws_final = workspace(IDX_OP_TOPK, nq, max(self.kb * BLOCK, 1), k, device=d)
 
     def run(self, stream=None, events=None):
@@ -270,8 +269,8 @@ class PrefillPlan:
                        group=dv.group, block_max=self.block_max, stream=stream)
         if events is not None:
             events[1].record()
-        idx_topk(self.block_max, self.nb, self.k, self.top_blocks, self.ws_blocks, n_valid=self.n_blocks,
-                 stream=stream)
+        idx_top_blocks(self.block_max, dv.n_vis, dv.max_n, self.k, self.top_blocks, self.block_count, self.ws_blocks,
+                       stream=stream)
         idx_score_pool_gather(dv.k_codes, dv.k_scales, dv.k_base, dv.n_vis, self.top_blocks, self.block_count,
                               self.kb, self.q_codes, self.q_scales, dv.w[0], self.cand_scores, stream=stream)
         idx_topk(self.cand_scores, self.kb * BLOCK, self.k, self.topk, self.ws_final, out_val=self.topk_val,
