@@ -1,16 +1,19 @@
 #!/usr/bin/env python3
-"""Benchmark: one decode step of the FP4 lightning indexer at 1M context on one MI355X.
+"""Benchmark: the FP4 lightning indexer's decode hot path at 1M context on one MI355X.
 
-Workload ("fullscan_1m"): 8 sequences x 2^20 visible compressed keys (decoder, m = 1), one
-query each, 32 heads x 128 dims, MXFP4 queries and keys, synthetic seeded inputs. One step is the
-whole hot path for that batch: quantise the Full layer's queries, scan every key (block-8
+Headline workload ("fullscan_1m"): 8 sequences x 2^20 visible compressed keys (decoder, m = 1),
+one query each, 32 heads x 128 dims, MXFP4 queries and keys, synthetic seeded inputs. One step is
+the whole hot path for that batch: quantise the Full layer's queries, scan every key (block-8
 maxima fused), build the candidate pool (pin + top-2048 blocks), take the Full layer's top-512,
 then 4 Reindex layers (quantise their queries, gather-score the pool, top-512 each).
 
 Prints one JSON line: entries scored per second over the step (Full-layer keys + pooled keys of
 the Reindex layers), top-512 queries per second, the scan kernel's HBM roofline fraction
-(achieved from HIP events around the scan launches of the timed steps), and the CPU oracle timed
-on a bounded sample of the same workload.
+(achieved from HIP events around the scan launches of the timed steps), the same step cold (1 GiB
+written before each repetition, outside its events) and the pool gather cold and warm, a record
+for each other configuration of the problem statement (configs: decode_32k, decode_batch64,
+reindex_1m, fullscan_512k, prefill_128k, each warm and cold with the roofline of its dominant
+kernel), and the CPU oracle timed on all host cores on the step's work.
 """
 from __future__ import annotations
 
@@ -55,53 +58,189 @@ def measured_traffic(record: str) -> int | None:
         return None
 
 
-def cpu_baseline(wl, max_queries: int = 8, max_keys: int = 1 << 19) -> dict:
-    """The oracle (plain C, threaded over queries) on a bounded sample: the Full layer of the
-    first min(8, cores) queries of the same workload (score every visible key, top-512, block
-    maxima, pin, pool), each over its first min(n, 2^19) visible keys so that the sample stays
-    within tens of seconds on slow hosts. The oracle quantises those keys first (untimed)."""
+def host_threads() -> int:
+    """threads for the CPU baseline: every core the process may use (the machine's CPU share, as
+    OMP_NUM_THREADS states it when set)"""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, target_s: float = 5.0, runs: int = 3, chunk: int = 1 << 14) -> dict:
+    """The oracle (plain C, as it stands) on all host cores, timed on the same work as the GPU
+    step: the Full layer of every query (score all visible keys, top-512, block maxima, pin,
+    top-2048 pool) and the Reindex layers (score the pooled keys with each layer's query,
+    top-512). Threads take (query, key-chunk) units of the Full layer, then one query per unit
+    for the selections and the Reindex layers. When the whole step would take longer than about
+    `target_s` per run, each query's Full layer covers only its first 2^-m of its visible keys
+    (halved until it fits); its cost is linear in that length. The Reindex layers' units run
+    side by side (their queries are all present in the synthetic workload). The oracle quantises the
+    keys first (untimed setup, as the GPU's key cache is); the queries are quantised inside the
+    timed region, as on the GPU. Median of `runs` runs."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import oracle
 
-    cores = os.cpu_count() or 1
-    nqs = max(1, min(max_queries, wl.nq, cores))
+    threads = host_threads()
     s = wl.signs()
-    seqs = sorted(set(int(b) for b in wl.qseq[:nqs]))
-    log(f"cpu baseline: oracle quantises the keys of {len(seqs)} sequence(s) (untimed)")
-    kcs, kss, seq_off, off = [], [], {}, 0
-    for b in seqs:
-        kc, ks = oracle.quantize(wl.keys(b, 0, min(int(wl.seq_len[b]), max_keys)), s, nthreads=cores)
-        kcs.append(kc)
-        kss.append(ks)
-        seq_off[b] = off
-        off += kc.shape[0]
-    kc = np.concatenate(kcs)
-    ks = np.concatenate(kss)
-    qc, qs = oracle.quantize(wl.q(0, range(nqs)), s)
-    w = wl.w(0, range(nqs))
-    n = np.minimum(wl.n_vis[:nqs].astype(np.int64), max_keys)
-    base = np.array([seq_off[int(b)] for b in wl.qseq[:nqs]], dtype=np.int64)
-    log(f"cpu baseline: timing the oracle Full layer on {nqs} queries with {nqs} threads")
-    t0 = time.perf_counter()
-    oracle.decode_batch(kc, ks, base, n, qc, qs, w, k=wl.k, nthreads=nqs)
-    dt = time.perf_counter() - t0
-    entries = int(n.sum())
-    return {"value": entries / dt, "unit": "entries/s", "cores": nqs, "kind": "oracle",
-            "sample": f"Full layer (score all keys, top-512, block max, pin, top-2048 pool) of {nqs} of the "
-                      f"{wl.nq} queries, each over its first {int(n[0])} visible keys; {dt:.2f} s wall on "
-                      f"{nqs} threads",
-            "seconds": round(dt, 3)}
+    nq, layers = wl.nq, wl.layers
+    qraw = [wl.q(layer) for layer in range(layers + 1)]
+    wraw = [wl.w(layer) for layer in range(layers + 1)]
+    # calibration: one chunk of keys per thread, all threads at once (wall time per key scored)
+    kc0, ks0 = oracle.quantize(wl.keys(int(wl.qseq[0]), 0, chunk), s, nthreads=threads)
+    qc0, qs0 = oracle.quantize(qraw[0][0], s)
+    with ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda _: oracle.score_rows(qc0, qs0, wraw[0][0], kc0, ks0), range(threads)))
+        per_key = (time.perf_counter() - t0) / (chunk * threads) * threads
+    full = int(max(wl.n_vis))
+    keys_per_q = full
+    def est(m):  # seconds of scoring per run on all threads
+        nn = np.minimum(wl.n_vis, m).astype(np.float64)
+        return float(nn.sum() + layers * np.minimum(nn, 8 * wl.topk_blocks).sum()) * per_key / threads
+
+    while keys_per_q > chunk and est(keys_per_q) > target_s:
+        keys_per_q //= 2
+    n = np.minimum(wl.n_vis.astype(np.int64), keys_per_q)
+    log(f"cpu baseline: {threads} threads, {per_key * 1e6:.1f} us per key per thread (all threads busy); Full layer over "
+        f"{keys_per_q} keys per query; oracle quantises the keys (untimed)")
+    kc, ks = {}, {}
+    for b in sorted(set(int(x) for x in wl.qseq)):
+        kc[b], ks[b] = oracle.quantize(wl.keys(b, 0, int(n[list(wl.qseq).index(b)])), s, nthreads=threads)
+
+    def one_run():
+        t_start = time.perf_counter()
+        qz = [oracle.quantize(qraw[layer], s, nthreads=threads) for layer in range(layers + 1)]
+        I = [np.empty(int(n[t])) for t in range(nq)]
+        A = [np.empty(int(n[t])) for t in range(nq)]
+
+        def full_unit(u):
+            t, c0 = u
+            b = int(wl.qseq[t])
+            c1 = min(int(n[t]), c0 + chunk)
+            I[t][c0:c1], A[t][c0:c1] = oracle.score_rows(qz[0][0][t], qz[0][1][t], wraw[0][t], kc[b][c0:c1],
+                                                         ks[b][c0:c1])
+
+        def select(t):
+            top = oracle.topk(I[t], wl.k)
+            pool = oracle.pool(oracle.block_max(I[t], 8), int(n[t]), 8, wl.topk_blocks)
+            return top, pool
+
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(full_unit, [(t, c0) for t in range(nq) for c0 in range(0, int(n[t]), chunk)]))
+            sel = list(ex.map(select, range(nq)))
+
+            def reindex(u):
+                layer, t = u
+                b = int(wl.qseq[t])
+                oracle.reindex_gather(qz[layer][0][t], qz[layer][1][t], wraw[layer][t], kc[b][:int(n[t])],
+                                      ks[b][:int(n[t])], sel[t][1], 8, wl.k)
+                return int(min(8 * len(sel[t][1]), int(n[t])))
+
+            entries = int(n.sum()) + sum(ex.map(reindex, [(l, t) for l in range(1, layers + 1) for t in range(nq)]))
+        return time.perf_counter() - t_start, entries
+
+    res = [one_run() for _ in range(runs)]
+    secs = sorted(r[0] for r in res)
+    dt = secs[len(secs) // 2]
+    entries = res[0][1]
+    sub = "every visible key" if keys_per_q >= full else f"the first {keys_per_q} visible keys"
+    return {"value": entries / dt, "unit": "entries/s", "cores": threads, "kind": "oracle",
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(),
+            "sample": f"the step's work for all {nq} queries: Full layer over {sub} of each query (score, top-512, "
+                      f"block max, pin, top-2048 pool), then {layers} Reindex layers scoring the pooled keys "
+                      f"(top-512 each); {entries} entries scored per run; median of {runs} runs "
+                      f"({', '.join(f'{x:.2f}' for x in secs)} s) on {threads} threads",
+            "seconds": round(dt, 3), "entries_per_run": entries}
 
 
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak, published
+FLUSH_BYTES = 1 << 30
 
 
-def bench_prefill(wl, args) -> int:
+class Flusher:
+    """Before each cold repetition, outside its event pair: writes 1 GiB of device memory with a
+    plain fill kernel (a changing non-zero byte, so never a memset), then reads it back with a
+    reduction. The 4 MB L2s and the 256 MB last-level cache then hold none of the workload's
+    inputs, and the lines they do hold are clean, so the measured kernel's misses do not also pay
+    for writing the flush's dirty lines back."""
+
+    def __init__(self):
+        import torch
+
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.v = 0
+
+    def __call__(self):
+        import torch
+
+        self.v = self.v % 250 + 1
+        self.buf.fill_(self.v)
+        self.buf.view(torch.int64).sum()
+
+
+def host_ahead():
+    """An untimed spin kernel of about 0.3 ms before a warm timed region, so that the host has
+    enqueued the timed launches before the GPU reaches them (small steps are otherwise bound by
+    the host's launch rate rather than by the device)."""
+    import torch
+
+    torch.cuda._sleep(700_000)
+
+
+def _pair():
+    import torch
+
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def _ms(pairs):
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2] if xs else float("nan")
+
+
+def hbm_roofline(bytes_per_launch: int, ms: float, kernel: str, traffic=None) -> dict:
+    achieved = bytes_per_launch / (ms / 1000.0) / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": kernel,
+            "algorithmic_bytes_per_launch": bytes_per_launch, "launch_ms": ms}
+
+
+def mfma_roofline(flop: float, ms: float, kernel: str, traffic=None, bytes_per_launch=None) -> dict:
+    achieved = flop / (ms / 1000.0) / 1e12
+    r = {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+         "frac": achieved / MFMA_FP4_PEAK_TFLOPS, "traffic": traffic, "kernel": kernel,
+         "algorithmic_flop_per_launch": flop, "launch_ms": ms}
+    if bytes_per_launch is not None:
+        r["algorithmic_bytes_per_launch"] = bytes_per_launch
+        r["hbm_achieved_gbs"] = bytes_per_launch / (ms / 1000.0) / 1e9
+        r["hbm_frac"] = r["hbm_achieved_gbs"] / HBM_PEAK_GBS
+    return r
+
+
+def prefill_record(wl, reps: int, warmup: int, flush) -> dict:
     """Chunked prefill: 4096 consecutive queries on 131072 keys, causal; the step is quantise q,
     the many-query scan (block maxima), top-512 blocks per query, re-score of those 4096 keys,
-    final top-512. The roofline is the scan's FP4 matrix throughput."""
-    import numpy as np
+    final top-512. The roofline is the scan's FP4 matrix throughput. Warm: steps back to back;
+    cold: the caches flushed before each step."""
     import torch
 
     from top_fp4_lightning_amd import pipeline
@@ -112,30 +251,51 @@ def bench_prefill(wl, args) -> int:
     log(f"workload {wl.name}: {wl.nq} queries, {wl.total_keys} keys; setup {time.perf_counter() - t:.1f} s")
     plan = pipeline.PrefillPlan(dev)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         plan.run()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        plan.run(events=evs[i])
+    scan_w = [_pair() for _ in range(reps)]
+    whole = _pair()
+    host_ahead()
+    whole[0].record(stream)
+    for i in range(reps):
+        plan.run(events=scan_w[i])
+    whole[1].record(stream)
     torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1000.0 / args.steps
-    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    step_cold, scan_c = [_pair() for _ in range(reps)], [_pair() for _ in range(reps)]
+    for i in range(reps):
+        flush()
+        step_cold[i][0].record(stream)
+        plan.run(events=scan_c[i])
+        step_cold[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms_warm = whole[0].elapsed_time(whole[1]) / reps
+    ms_cold = _median(_ms(step_cold))
+    scan_warm, scan_cold = sum(_ms(scan_w)) / reps, _median(_ms(scan_c))
     pairs = int(wl.n_vis.sum())
     flop = 2.0 * 4096.0 * pairs
-    achieved = flop / (scan_ms / 1000.0) / 1e12
+    sb = int(wl.total_keys) * 68 + wl.nq * (32 * 68 + 32 * 4) + int(sum((n + 7) // 8 for n in wl.n_vis)) * 4
+    rec = {"workload": "prefill_128k: 4096 queries x 131072 keys, causal (query i sees <= 126976+i)",
+           "metric": "(query, key) pairs scored/s, top-512 queries/s; % of FP4 MFMA roofline",
+           "reps": reps, "ms_per_step": ms_warm, "ms_per_step_cold": ms_cold,
+           "pairs_per_s": pairs / (ms_warm / 1000.0), "pairs_per_s_cold": pairs / (ms_cold / 1000.0),
+           "queries_per_s": wl.nq / (ms_warm / 1000.0), "scan_ms": scan_warm, "scan_ms_cold": scan_cold,
+           "roofline": mfma_roofline(flop, scan_warm, "score_multi_kernel",
+                                     measured_traffic("score_multi_prefill_128k_traffic"), sb),
+           "roofline_cold": mfma_roofline(flop, scan_cold, "score_multi_kernel", None, sb)}
+    del plan, dev
+    torch.cuda.empty_cache()
+    return rec
+
+
+def bench_prefill(wl, args) -> int:
+    rec = prefill_record(wl, args.steps, args.warmup, Flusher())
     print(json.dumps({
         "metric": "prefill (query, key) pairs scored/s; % of FP4 MFMA roofline",
-        "value": pairs / (ms_step / 1000.0), "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "value": rec["pairs_per_s"], "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp4", "data": "synthetic",
-        "config": {"workload": "prefill_128k: 4096 queries x 131072 keys, causal (query i sees <= 126976+i)"},
-        "queries_per_s": wl.nq / (ms_step / 1000.0), "scan_ms": scan_ms,
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_FP4_PEAK_TFLOPS,
-                     "traffic": measured_traffic("score_multi_prefill_128k_traffic"), "kernel": "score_multi_kernel",
-                     "algorithmic_flop_per_launch": flop},
+        "config": {"workload": rec["workload"]}, **{k: v for k, v in rec.items() if k not in ("workload", "metric")},
     }), flush=True)
     return 0
 
@@ -143,83 +303,189 @@ def bench_prefill(wl, args) -> int:
 DECODE_CONFIGS = {
     "fullscan_1m": "fullscan_1m decode step: batch 8 x 1048576 keys (m=1), Full scan + top-512 + "
                    "pool(2048 blocks of 8) + 4 Reindex layers",
+    "fullscan_512k": "fullscan_512k decode step: batch 8 x 524288 keys (encoder shape, m=2), Full scan + "
+                     "top-512 + pool(2048 blocks of 8)",
+    "decode_32k": "decode_32k: 1 query x 32768 keys, Full scan + top-512 + pool(2048 of 4096 blocks)",
+    "decode_batch64": "decode_batch64: 64 sequences x U[65536, 131072] keys, Full scan + top-512 + "
+                      "pool(2048 blocks of 8)",
+    "reindex_1m": "reindex_1m: 64 sequences x 1048576 keys, Full pass + pool(2048 blocks of 8) + 4 Reindex "
+                  "layers gathering the 16384 pooled keys, top-512 each",
     "spec_decode_1m": "spec_decode_1m verify step: batch 8 x 1048576 keys (m=1), 6 positions per sequence "
                       "(token + 5 draft), Full scan + top-512 + pool(2048 blocks of 8) + 4 Reindex layers",
 }
+
+
+class DecodeStep:
+    """One decode step through the plan (quantise, Full scan, pool, Full top-512 through the
+    pool, then per Reindex layer quantise, gather, top-512), with optional HIP event pairs
+    around the scan and around each gather launch (recorded on the launch stream)."""
+
+    def __init__(self, wl):
+        import torch
+
+        from top_fp4_lightning_amd import pipeline
+
+        t = time.perf_counter()
+        self.wl = wl
+        self.dev = pipeline.DeviceWorkload.from_workload(wl)
+        torch.cuda.synchronize()
+        log(f"workload {wl.name}: {wl.nq} queries, {wl.total_keys} keys, {wl.layers} Reindex layers; "
+            f"setup {time.perf_counter() - t:.1f} s")
+        self.plan = pipeline.DecodePlan(self.dev)
+        self.stream = torch.cuda.current_stream()
+        n_vis = [int(x) for x in wl.n_vis]
+        self.n_vis = n_vis
+        self.pool_pos = int(sum(min(n, 8 * min(2048, (n + 7) // 8)) for n in n_vis))
+        self.entries = int(sum(n_vis)) + self.plan.layers * self.pool_pos
+        self.queries = wl.nq * (1 + self.plan.layers)
+        self.slots = wl.nq * self.plan.max_blocks * 8
+        # gather: 68 B per pooled key, q (32 x 68 B) + w (128 B) per query, 4 B per score slot written
+        self.gather_bytes = self.pool_pos * 68 + wl.nq * (32 * 68 + 32 * 4) + self.slots * 4
+
+    def __call__(self, scan_ev=None, gather_ev=None, flush=None):
+        p = self.plan
+        p.quantize(0)
+        if scan_ev is not None:
+            scan_ev[0].record(self.stream)
+        p.full_scan()
+        if scan_ev is not None:
+            scan_ev[1].record(self.stream)
+        p.build_pool()
+        for layer in range(p.layers + 1):
+            if layer:
+                p.quantize(layer)
+            if flush is not None:
+                flush()
+            p.pool_select(layer, events=None if gather_ev is None else gather_ev[layer])
+
+    def scan_roofline(self, ms: float, traffic=None) -> dict:
+        wl, dev = self.wl, self.dev
+        if dev.group == 1:
+            return hbm_roofline(scan_bytes(self.n_vis, wl.nq), ms, "score_full_kernel", traffic)
+        flop = 2.0 * 4096.0 * float(sum(self.n_vis))
+        groups = [self.n_vis[i:i + dev.group] for i in range(0, len(self.n_vis), dev.group)]
+        sb = (sum(max(g) * 68 for g in groups) + wl.nq * (32 * 68 + 32 * 4) +
+              sum((n + 7) // 8 for n in self.n_vis) * 4)
+        return mfma_roofline(flop, ms, "score_multi_kernel", traffic, sb)
+
+    def measure(self, reps: int, warmup: int, flush) -> dict:
+        """warm (steps back to back) and cold (caches flushed before each step) step times, the
+        scan's launch time in both, and the pool gather per layer: cold (caches flushed right
+        before the gather launch) and warm (gathers launched back to back)"""
+        import torch
+
+        p, L = self.plan, self.plan.layers
+        for _ in range(warmup):
+            self()
+        torch.cuda.synchronize()
+        scan_w = [_pair() for _ in range(reps)]
+        whole = _pair()
+        host_ahead()
+        whole[0].record(self.stream)
+        for i in range(reps):
+            self(scan_ev=scan_w[i])
+        whole[1].record(self.stream)
+        torch.cuda.synchronize()
+        step_c, scan_c = [_pair() for _ in range(reps)], [_pair() for _ in range(reps)]
+        for i in range(reps):
+            flush()
+            step_c[i][0].record(self.stream)
+            self(scan_ev=scan_c[i])
+            step_c[i][1].record(self.stream)
+        torch.cuda.synchronize()
+        g_cold = [[_pair() for _ in range(L + 1)] for _ in range(reps)]
+        for i in range(reps):
+            self(gather_ev=g_cold[i], flush=flush)
+        g_warm = _pair()
+        host_ahead()
+        g_warm[0].record(self.stream)
+        for _ in range(reps):
+            for layer in range(L + 1):
+                p.pool_gather(layer)
+        g_warm[1].record(self.stream)
+        torch.cuda.synchronize()
+        ms_warm = whole[0].elapsed_time(whole[1]) / reps
+        ms_cold = _median(_ms(step_c))
+        scan_warm, scan_cold = sum(_ms(scan_w)) / reps, _median(_ms(scan_c))
+        gc = _median([x for row in g_cold for x in _ms(row)])
+        gw = g_warm[0].elapsed_time(g_warm[1]) / (reps * (L + 1))
+        gb = self.gather_bytes
+        return {"reps": reps, "ms_per_step": ms_warm, "ms_per_step_cold": ms_cold,
+                "entries_per_s": self.entries / (ms_warm / 1000.0),
+                "entries_per_s_cold": self.entries / (ms_cold / 1000.0),
+                "top512_queries_per_s": self.queries / (ms_warm / 1000.0),
+                "top512_queries_per_s_cold": self.queries / (ms_cold / 1000.0),
+                "full_scan_entries_per_s": sum(self.n_vis) / (scan_warm / 1000.0),
+                "scan_ms": scan_warm, "scan_ms_cold": scan_cold,
+                "gather": {"kernel": "score_gather_kernel", "algorithmic_bytes_per_launch": gb,
+                           "ms_cold": gc, "frac_cold": gb / (gc / 1000.0) / 1e9 / HBM_PEAK_GBS,
+                           "ms_warm": gw, "frac_warm": gb / (gw / 1000.0) / 1e9 / HBM_PEAK_GBS,
+                           "cold_protocol": "1 GiB written and read back right before each gather launch, one event pair "
+                                            "per launch",
+                           "warm_protocol": "every layer's gather launched back to back between one event pair"}}
+
+
+def decode_record(name: str, reps: int, warmup: int, flush) -> dict:
+    import torch
+
+    import synth
+
+    wl = synth.config(name)
+    st = DecodeStep(wl)
+    m = st.measure(reps, warmup, flush)
+    traffic = measured_traffic("score_full_fullscan_1m_traffic") if name == "fullscan_1m" else None
+    rec = {"workload": DECODE_CONFIGS.get(name, name), **m,
+           "roofline": st.scan_roofline(m["scan_ms"], traffic), "roofline_cold": st.scan_roofline(m["scan_ms_cold"])}
+    if name == "reindex_1m":
+        # the Reindex layers' gather is this workload's headline kernel (HBM on gathered bytes)
+        g = m["gather"]
+        rec["gather"]["traffic"] = measured_traffic("score_gather_reindex_1m_traffic")
+        rec["roofline_gather_cold"] = hbm_roofline(st.gather_bytes, g["ms_cold"], "score_gather_kernel",
+                                                   rec["gather"]["traffic"])
+        rec["roofline_gather_warm"] = hbm_roofline(st.gather_bytes, g["ms_warm"], "score_gather_kernel",
+                                                   rec["gather"]["traffic"])
+        rec["reindex_queries_per_s"] = wl.nq * wl.layers / (m["ms_per_step"] / 1000.0)
+    del st
+    torch.cuda.empty_cache()
+    return rec
 
 
 def bench_decode(wl, args) -> int:
     """One decode step per timed iteration (quantise, Full scan, pool, Full top-512 through the
     pool, Reindex layers). With one query per sequence the Full scan is the single-query kernel
     and the roofline is HBM; with several positions per sequence (speculative verification) it is
-    the many-query kernel and the roofline is FP4 MFMA."""
-    import numpy as np
+    the many-query kernel and the roofline is FP4 MFMA.
+
+    The timed region follows the bench contract: `warmup` untimed steps, then exactly `steps`
+    steps back to back between two synchronisations (the wall clock gives ms_per_step); HIP events
+    on the launch stream around each scan launch give the scan's roofline. Afterwards, outside
+    that region, the same plan is measured warm and cold (DecodeStep.measure), and in the default
+    run every other configuration gets its own record (configs)."""
     import torch
 
-    from top_fp4_lightning_amd import pipeline
-
-    t = time.perf_counter()
-    dev = pipeline.DeviceWorkload.from_workload(wl)
-    torch.cuda.synchronize()
-    log(f"workload {wl.name}: {wl.nq} queries, {wl.total_keys} keys, {wl.layers} Reindex layers; "
-        f"setup {time.perf_counter() - t:.1f} s")
-    plan = pipeline.DecodePlan(dev)
-    stream = torch.cuda.current_stream()
-
-    def step(ev=None, gev=None):
-        plan.quantize(0)
-        if ev is not None:
-            ev[0].record(stream)
-        plan.full_scan()
-        if ev is not None:
-            ev[1].record(stream)
-        plan.build_pool()
-        plan.pool_select(0, events=gev)
-        for layer in range(1, plan.layers + 1):
-            plan.quantize(layer)
-            plan.pool_select(layer)
-
+    st = DecodeStep(wl)
+    plan = st.plan
     for _ in range(args.warmup):
-        step()
+        st()
     torch.cuda.synchronize()
-    def pair():
-        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    evs = [pair() for _ in range(args.steps)]
+    evs = [_pair() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        st(scan_ev=evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1000.0 / args.steps
-    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-
-    # The pool gather, timed outside the timed steps. Cold: the Full layer's gather right after
-    # the scan, whose stream has replaced the cache contents, so its pooled blocks come from HBM
-    # (one event pair per launch, which adds the events' own few microseconds). Warm: the same
-    # gather launched back to back between one event pair, its blocks in the last-level cache, as
-    # for Reindex layers that follow one another with nothing in between.
-    gevs = [pair() for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(None, gevs[i])
-    burst = pair()
-    burst[0].record(stream)
-    for _ in range(args.steps):
-        plan.pool_gather(0)
-    burst[1].record(stream)
-    torch.cuda.synchronize()
-    gather_cold_ms = float(np.mean([a.elapsed_time(b) for a, b in gevs]))
-    gather_warm_ms = burst[0].elapsed_time(burst[1]) / args.steps
+    scan_ms = sum(_ms(evs)) / args.steps
     ms_eager = ms_step
     if args.graph:
         # the whole step captured once in a HIP graph (the plan allocates nothing and the library
         # issues no memsets) and replayed: no per-launch host work inside the timed region
         side = torch.cuda.Stream()
-        side.wait_stream(stream)
+        side.wait_stream(st.stream)
         with torch.cuda.stream(side):
             plan.run(stream=side)
-        stream.wait_stream(side)
+        st.stream.wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
@@ -232,39 +498,12 @@ def bench_decode(wl, args) -> int:
             graph.replay()
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t0) * 1000.0 / args.steps
-
-    n_vis = [int(x) for x in wl.n_vis]
-    pool_pos = int(sum(min(n, 8 * min(2048, (n + 7) // 8)) for n in n_vis))
-    entries = int(sum(n_vis)) + plan.layers * pool_pos
-    queries = wl.nq * (1 + plan.layers)
-    if dev.group == 1:
-        sb = scan_bytes(n_vis, wl.nq)
-        achieved = sb / (scan_ms / 1000.0) / 1e9
-        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": achieved / HBM_PEAK_GBS,
-                    "traffic": measured_traffic("score_full_fullscan_1m_traffic") if wl.name == "fullscan_1m" else None,
-                    "kernel": "score_full_kernel", "algorithmic_bytes_per_launch": sb}
-    else:
-        # many-query scan: keys are read once per group, the matrix work grows with the positions
-        flop = 2.0 * 4096.0 * float(sum(n_vis))
-        groups = [n_vis[i:i + dev.group] for i in range(0, len(n_vis), dev.group)]
-        sb = sum(max(g) * 68 for g in groups) + wl.nq * (32 * 68 + 32 * 4) + sum((n + 7) // 8 for n in n_vis) * 4
-        achieved = flop / (scan_ms / 1000.0) / 1e12
-        roofline = {"bound": "mfma", "achieved": achieved, "peak": MFMA_FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / MFMA_FP4_PEAK_TFLOPS, "traffic": None, "kernel": "score_multi_kernel",
-                    "algorithmic_flop_per_launch": flop, "algorithmic_bytes_per_launch": sb,
-                    "hbm_achieved_gbs": sb / (scan_ms / 1000.0) / 1e9,
-                    "hbm_frac": sb / (scan_ms / 1000.0) / 1e9 / HBM_PEAK_GBS}
-    # gather: 68 B per pooled key, q (32 x 68 B) + w (128 B) per query, 4 B per score slot written
-    slots = wl.nq * plan.max_blocks * 8
-    gb = pool_pos * 68 + wl.nq * (32 * 68 + 32 * 4) + slots * 4
-    gather = {"kernel": "score_gather_kernel", "algorithmic_bytes_per_launch": gb,
-              "ms_cold": gather_cold_ms, "hbm_frac_cold": gb / (gather_cold_ms / 1000.0) / 1e9 / HBM_PEAK_GBS,
-              "ms_warm": gather_warm_ms, "frac_warm": gb / (gather_warm_ms / 1000.0) / 1e9 / HBM_PEAK_GBS,
-              "traffic": measured_traffic("score_gather_reindex_1m_traffic") if wl.name == "reindex_1m" else None}
+    flush = Flusher()
+    extra = st.measure(min(args.steps, 20), 1, flush)
+    traffic = measured_traffic("score_full_fullscan_1m_traffic") if wl.name == "fullscan_1m" else None
     res = {
         "metric": "indexer entries scored/s + top-512 queries/s at 1M ctx; % of HBM roofline",
-        "value": entries / (ms_step / 1000.0),
+        "value": st.entries / (ms_step / 1000.0),
         "unit": "entries/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -276,16 +515,29 @@ def bench_decode(wl, args) -> int:
         "dtype": "mxfp4",
         "data": "synthetic (seeded N(0,1) bf16 q/k, N(0,1/32) w, 1% planted keys; no trained weights)",
         "config": {"workload": DECODE_CONFIGS.get(wl.name, wl.name),
-                   "batch": wl.nseq, "positions_per_sequence": dev.group, "context": int(wl.seq_len[0]),
+                   "batch": wl.nseq, "positions_per_sequence": st.dev.group, "context": int(wl.seq_len[0]),
                    "reindex_layers": plan.layers, "k": 512, "pool_blocks": 2048, "block": 8},
-        "top512_queries_per_s": queries / (ms_step / 1000.0),
-        "full_scan_entries_per_s": int(sum(n_vis)) / (scan_ms / 1000.0),
+        "top512_queries_per_s": st.queries / (ms_step / 1000.0),
+        "full_scan_entries_per_s": int(sum(st.n_vis)) / (scan_ms / 1000.0),
         "scan_ms": scan_ms,
         "step_launch": "hip graph replay" if args.graph else "eager launches",
         "ms_per_step_eager": ms_eager,
-        "roofline": roofline,
-        "gather": gather,
+        "roofline": st.scan_roofline(scan_ms, traffic),
+        "cold": {"protocol": "1 GiB written and read back before each repetition, outside its event pair",
+                 "ms_per_step": extra["ms_per_step_cold"], "entries_per_s": extra["entries_per_s_cold"],
+                 "scan_ms": extra["scan_ms_cold"], "roofline": st.scan_roofline(extra["scan_ms_cold"])},
+        "gather": extra["gather"],
     }
+    del st, plan
+    torch.cuda.empty_cache()
+    if args.all_configs:
+        import synth
+
+        configs = {}
+        for name in ("decode_32k", "decode_batch64", "reindex_1m", "fullscan_512k"):
+            configs[name] = decode_record(name, args.config_reps, 2, flush)
+        configs["prefill_128k"] = prefill_record(synth.config("prefill_128k"), args.config_reps, 2, flush)
+        res["configs"] = configs
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)
@@ -488,6 +740,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="fullscan_1m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--config-reps", type=int, default=10,
+                    help="repetitions of each other configuration's record (warm and cold)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the records of the other configurations")
     ap.add_argument("--graph", action="store_true",
                     help="decode workloads: time replays of the step captured in a HIP graph")
     ap.add_argument("--copy-probe", action="store_true",
@@ -524,6 +780,7 @@ def main() -> int:
     wl = synth.config(args.workload)
     if args.workload == "prefill_128k":
         return bench_prefill(wl, args)
+    args.all_configs = args.workload == "fullscan_1m" and not args.headline_only
     return bench_decode(wl, args)
 
 if __name__ == "__main__":

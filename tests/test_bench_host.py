@@ -64,3 +64,16 @@ def test_committed_traffic_records_are_current(name):
     assert bench.measured_traffic(name) == rec["traffic_bytes_per_launch"]
     # never below the bytes the kernel must move
     assert rec["traffic_bytes_per_launch"] >= 0.99 * rec["algorithmic_bytes_per_launch"]
+
+
+def test_cpu_baseline_reports_cores_model_and_median():
+    import synth
+
+    wl = synth.decode_workload("cpu", 9, [20000, 17001], layers=1)
+    r = bench.cpu_baseline(wl, target_s=0.5, runs=3)
+    assert r["kind"] == "oracle" and r["unit"] == "entries/s" and r["value"] > 0
+    assert r["cores"] == bench.host_threads() and r["nproc"] == os.cpu_count()
+    assert isinstance(r["cpu_model"], str) and r["cpu_model"]
+    assert "median of 3 runs" in r["sample"]
+    # the step's entries: every visible key of the Full layer plus the pooled keys of the Reindex layer
+    assert r["entries_per_run"] == 20000 + 17001 + min(20000, 16384) + min(17001, 16384)
