@@ -93,9 +93,9 @@ __device__ __forceinline__ float combine2(float p0, float p1) {
 // loads of block s, publishes block s and frees the buffer of block s - 1 for the next issue.
 // Control flow around the barriers is uniform per block.
 //
-// Block maxima: after a step, all eight lanes of a key block hold its maximum; lane 8g + s keeps
-// block g of step s (mod 8) in one register per query, and every eighth step (or at the wave's
-// last step) the wave writes the 64 maxima of those 8 steps with one 256-byte store.
+// Block maxima: after a step, all eight lanes of a key block hold its maximum, and lane 8g stores
+// that of block g (eight consecutive floats per step and query): no per-step bookkeeping on the
+// vector pipe, which bounds this kernel.
 constexpr int kStepKeys = 64;
 constexpr int kStageSteps = 2;                      // 64-key steps per staged block (one barrier)
 constexpr int kStageCodes = kStepKeys * kRowBytes;  // bytes of codes per step
@@ -215,16 +215,29 @@ __global__ __launch_bounds__(256) void score_multi_kernel(ScoreArgs a) {
     const int last = (nmax - e_begin + kStepKeys - 1) / kStepKeys < n_steps
                          ? (nmax - e_begin + kStepKeys - 1) / kStepKeys - 1
                          : n_steps - 1;
-    float bacc[QW];
+    // lane 8g of a step stores the maximum of block g, through a buffer descriptor of the query's
+    // row: the lane's byte offset is fixed, the step's (8 blocks a step) is a scalar
+    const bool bm_lane = (lane & 7) == 0;
+    __amdgpu_buffer_rsrc_t bm_rsrc[QW];
 #pragma unroll
-    for (int i = 0; i < QW; ++i) bacc[i] = -INFINITY;
+    for (int i = 0; i < QW; ++i)
+        bm_rsrc[i] = __builtin_amdgcn_make_buffer_rsrc(BMAX ? (void*)brow[i] : (void*)a.k_codes, 0,
+                                                       BMAX ? (int)(((nq_[i] + kBlock - 1) / kBlock) * 4) : 0,
+                                                       kRsrcWord3);
+    const int bm_voff = ((e_begin >> 3) + (lane >> 3)) * 4;
+    // score rows the same way: lane l stores key e0 + l, keys past the query's count are dropped
+    __amdgpu_buffer_rsrc_t sc_rsrc[QW];
+#pragma unroll
+    for (int i = 0; i < QW; ++i)
+        sc_rsrc[i] = __builtin_amdgcn_make_buffer_rsrc(SCORES ? (void*)srow[i] : (void*)a.k_codes, 0,
+                                                       SCORES ? nq_[i] * 4 : 0, kRsrcWord3);
+    const int sc_voff = (e_begin + lane) * 4;
 
     // score step `it` for every query; MASKED steps drop keys past each query's count
     auto step = [&](const KTile32 (&t)[2], int it, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
         const int e0 = e_begin + it * kStepKeys;
         const int el = e0 + lane;
-        const bool flush = (it & 7) == 7 || it == last;  // uniform
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
             if (i >= qv) break;  // uniform per wave
@@ -232,16 +245,16 @@ __global__ __launch_bounds__(256) void score_multi_kernel(ScoreArgs a) {
             const v16f o1 = mfma_tile32(q[i], t[1]);
             const float sc = combine2(lane_partial32(q[i], o0), lane_partial32(q[i], o1));
             const bool valid = !MASKED || el < nq_[i];
-            if (SCORES && valid) srow[i][el] = sc;
+            if (SCORES)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), sc_rsrc[i], sc_voff, it * kStepKeys * 4, 0);
             if (BMAX) {
-                const float m = max8(valid ? sc : -INFINITY);
-                bacc[i] = (lane & 7) == (it & 7) ? m : bacc[i];
-                if (flush) {
-                    // lane 8g + s holds block g of step (it & ~7) + s
-                    const int s_ = lane & 7, g_ = lane >> 3;
-                    const int blk = (e_begin >> 3) + (it & ~7) * 8 + s_ * 8 + g_;
-                    if (s_ <= (it & 7) && blk < (nq_[i] + kBlock - 1) / kBlock) brow[i][blk] = bacc[i];
-                }
+                // every lane of a block holds its maximum; one lane per block stores it (the
+                // block is visible when its first key is)
+                float m = max8(valid ? sc : -INFINITY);
+                asm volatile("" : "+v"(m));  // the whole maximum in every lane, before the store branch
+                if (bm_lane)  // blocks past the query's visible ones fall outside the descriptor
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), bm_rsrc[i], bm_voff,
+                                                          it * (kStepKeys / kBlock) * 4, 0);
             }
             // one query's matrix results live at a time: keeps the wave within the register
             // budget of four waves per SIMD (other waves hide the matrix latency)
@@ -251,30 +264,37 @@ __global__ __launch_bounds__(256) void score_multi_kernel(ScoreArgs a) {
 
     const int n_stages = (n_steps + kStageSteps - 1) / kStageSteps;
     for (int sg = 0; sg < kBufs - 1 && sg < n_stages; ++sg) stage_issue(sg);
+    // staged block sg lives in buffer sg % kBufs: the loop is unrolled over the buffers, so that
+    // each copy reads its buffer at fixed LDS offsets (immediates of the operand reads)
 #pragma nounroll
-    for (int sg = 0; sg < n_stages; ++sg) {
-        // staged blocks issued after this one so far: their loads may stay in flight
-        const int younger = (n_stages - 1 < sg + kBufs - 2 ? n_stages - 1 : sg + kBufs - 2) - sg;
-        if (kBufs >= 4 && younger >= 2)
-            wait_vm<2 * kLoadsPerStage>();
-        else if (younger >= 1)
-            wait_vm<kLoadsPerStage>();
-        else
-            wait_vm<0>();
-        // every wave's loads of block sg have landed, and every wave is done with block sg - 1,
-        // whose buffer the next issue overwrites
-        __syncthreads();
-        if (sg + kBufs - 1 < n_stages) stage_issue(sg + kBufs - 1);
+    for (int sg0 = 0; sg0 < n_stages; sg0 += kBufs) {
 #pragma unroll
-        for (int ss = 0; ss < kStageSteps; ++ss) {
-            const int it = sg * kStageSteps + ss;
-            if (it <= last) {  // uniform per wave
-                KTile32 t[2];
-                read_tiles(sg % kBufs, ss, t);
-                if (e_begin + (it + 1) * kStepKeys <= nmin)
-                    step(t, it, std::false_type{});
-                else
-                    step(t, it, std::true_type{});
+        for (int buf = 0; buf < kBufs; ++buf) {
+            const int sg = sg0 + buf;
+            if (sg >= n_stages) break;  // uniform per block
+            // staged blocks issued after this one so far: their loads may stay in flight
+            const int younger = (n_stages - 1 < sg + kBufs - 2 ? n_stages - 1 : sg + kBufs - 2) - sg;
+            if (kBufs >= 4 && younger >= 2)
+                wait_vm<2 * kLoadsPerStage>();
+            else if (younger >= 1)
+                wait_vm<kLoadsPerStage>();
+            else
+                wait_vm<0>();
+            // every wave's loads of block sg have landed, and every wave is done with block sg - 1,
+            // whose buffer the next issue overwrites
+            __syncthreads();
+            if (sg + kBufs - 1 < n_stages) stage_issue(sg + kBufs - 1);
+#pragma unroll
+            for (int ss = 0; ss < kStageSteps; ++ss) {
+                const int it = sg * kStageSteps + ss;
+                if (it <= last) {  // uniform per wave
+                    KTile32 t[2];
+                    read_tiles(buf, ss, t);
+                    if (e_begin + (it + 1) * kStepKeys <= nmin)
+                        step(t, it, std::false_type{});
+                    else
+                        step(t, it, std::true_type{});
+                }
             }
         }
     }
