@@ -544,6 +544,58 @@ def bench_decode(wl, args) -> int:
     return 0
 
 
+def bench_select_ties(args) -> int:
+    """Selection on rows of tied values (a zero query scores every key 0): the decode top-512 shape
+    (8 rows of 16384 pool-order scores, k = 512) and the pool shape (8 rows of 131072 block maxima
+    of 2^20 positions, top-2048 with the pin), each on seeded normal rows, rows of one value and
+    rows of 97 distinct values, timed with HIP events per launch (median over the steps)."""
+    import numpy as np
+    import torch
+
+    import top_fp4_lightning_amd as fx
+
+    rng = np.random.default_rng(7)
+    stream = torch.cuda.current_stream()
+
+    def rows(kind, nq, n):
+        if kind == "normal":
+            return torch.from_numpy(rng.standard_normal((nq, n)).astype(np.float32)).cuda()
+        if kind == "equal":
+            return torch.zeros(nq, n, dtype=torch.float32, device="cuda")
+        return torch.from_numpy(rng.integers(0, 97, (nq, n)).astype(np.float32)).cuda()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        evs = [_pair() for _ in range(args.steps)]
+        for e in evs:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return _median(_ms(evs)) * 1000.0
+
+    res = {"metric": "selection time on tied rows, us per launch (median)", "steps": args.steps,
+           "warmup": args.warmup}
+    nq, n, k = 8, 16384, 512
+    ws = fx.workspace(fx.IDX_OP_TOPK, nq, n, k)
+    out = torch.empty(nq, k, dtype=torch.int32, device="cuda")
+    for kind in ("normal", "equal", "distinct97"):
+        v = rows(kind, nq, n)
+        res[f"topk_8x16384_k512_{kind}_us"] = timed(lambda: fx.idx_topk(v, n, k, out, ws))
+    npos = 1 << 20
+    nb = npos // 8
+    ws = fx.workspace(fx.IDX_OP_BUILD_POOL, nq, npos, 2048)
+    pb = torch.empty(nq, 2048, dtype=torch.int32, device="cuda")
+    pc = torch.empty(nq, dtype=torch.int32, device="cuda")
+    nv = torch.full((nq,), npos, dtype=torch.int32, device="cuda")
+    for kind in ("normal", "equal", "distinct97"):
+        v = rows(kind, nq, nb)
+        res[f"pool_8x131072_k2048_{kind}_us"] = timed(lambda: fx.idx_build_pool(v, nv, npos, pb, pc, ws))
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_mask_form(args) -> int:
     """The decode step at fullscan_1m in the pool's training form, all 5 layers batched: one
     many-query scan writes every layer's full score row (8 x 5 rows of 2^20), then the pool and a
@@ -777,6 +829,8 @@ def main() -> int:
         return bench_token(args)
     if args.workload == "mask_form_1m":
         return bench_mask_form(args)
+    if args.workload == "select_ties":
+        return bench_select_ties(args)
     wl = synth.config(args.workload)
     if args.workload == "prefill_128k":
         return bench_prefill(wl, args)

@@ -187,10 +187,24 @@ def adversarial_rows(rng, nq, n, kind, k):
         a = np.zeros((nq, n), np.float32)
         a[:, n // 3] = 1e30
         return a
+    if kind == "ties_below_k":  # fewer than k values above a value most of the row ties at
+        a = np.ones((nq, n), np.float32)
+        a[:, rng.choice(n, size=min(n, k // 2), replace=False)] = 5.0
+        return a
+    if kind == "ties_above_k":  # more than k values above a value most of the row ties at
+        a = np.ones((nq, n), np.float32)
+        a[:, rng.choice(n, size=min(n, k + 100), replace=False)] = rng.uniform(2.0, 3.0, min(n, k + 100))
+        return a
+    if kind == "ties_stacked":  # three tied levels: the top one clustered at the row start, so that
+        a = np.ones((nq, n), np.float32)  # some wavefronts bound below it and rounds of ties follow
+        a[rng.random((nq, n)) < 0.37] = 2.0
+        a[:, :min(n, 5000)] = 3.0
+        return a
     raise KeyError(kind)
 
 
-@pytest.mark.parametrize("kind", ["posinf_few", "posinf_many", "nan", "signed_zeros", "narrow", "sparse", "one_hot"])
+@pytest.mark.parametrize("kind", ["posinf_few", "posinf_many", "nan", "signed_zeros", "narrow", "sparse", "one_hot",
+                                  "ties_below_k", "ties_above_k", "ties_stacked"])
 @pytest.mark.parametrize("n,k", [(16384, 512), (5000, 1025), (3000, 1), (70000, 512), (200000, 2048), (40000, 64),
                                  (16384, 2048)])
 def test_topk_adversarial(fx, n, k, kind):
@@ -234,6 +248,41 @@ def test_topk_many_rows(fx, n, k):
         cnt = int((ref >= 0).sum())
         assert np.array_equal(out[t, :cnt], np.sort(ref[:cnt])), f"row {t}"
         assert (out[t, cnt:] == -1).all(), f"row {t}"
+
+
+@pytest.mark.parametrize("n,kind", [(16384 * 8, "equal"), (16385 * 8, "equal"), (1 << 20, "equal"),
+                                    (1 << 20, "few_distinct"), (1 << 20, "ties_below_k"), (100003, "ties_above_k")])
+def test_build_pool_ties(fx, n, kind):
+    """pools over rows of tied block maxima (a zero query gives all-equal rows): equal to the
+    oracle's full sort with ties to the lower block id, on both selection paths"""
+    rng = np.random.default_rng(n + len(kind))
+    nq = 3
+    nb = (n + 7) // 8
+    if kind == "equal":
+        bm = np.zeros((nq, nb), np.float32)
+    elif kind == "few_distinct":
+        bm = rng.integers(0, 97, (nq, nb)).astype(np.float32)
+    elif kind == "ties_below_k":
+        bm = np.ones((nq, nb), np.float32)
+        for t in range(nq):
+            bm[t, rng.choice(nb, size=1000, replace=False)] = 4.0
+    else:
+        bm = np.ones((nq, nb), np.float32)
+        for t in range(nq):
+            bm[t, rng.choice(nb, size=3000, replace=False)] = rng.uniform(2, 3, 3000)
+    nv = np.array([n, n - 5, (n * 3) // 4], np.int32)
+    ws = fx.workspace(fx.IDX_OP_BUILD_POOL, nq, n, 2048)
+    pb = torch.full((nq, 2048), -7, dtype=torch.int32, device="cuda")
+    pc = torch.empty(nq, dtype=torch.int32, device="cuda")
+    fx.idx_build_pool(torch.from_numpy(bm).cuda(), torch.from_numpy(nv).cuda(), n, pb, pc, ws)
+    torch.cuda.synchronize()
+    pb, pc = pb.cpu().numpy(), pc.cpu().numpy()
+    for t in range(nq):
+        nbt = (int(nv[t]) + 7) // 8
+        ref = oracle.pool(bm[t, :nbt].astype(np.float64), int(nv[t]), 8, 2048)
+        assert pc[t] == len(ref), (t, pc[t], len(ref))
+        assert np.array_equal(pb[t, :len(ref)], ref), t
+        assert (pb[t, len(ref):] == -1).all()
 
 
 @pytest.mark.parametrize("n", [1, 8, 9, 16383, 16384, 16385, 16392, 100003, 1 << 20])

@@ -482,6 +482,14 @@ __device__ __forceinline__ uint32_t wave_rth(uint32_t lo, uint32_t R) {
     return t;
 }
 
+// For t = wave_rth(lo, R) the R-th largest lane key lies in t's 16-bit bucket: the bucket's
+// smallest key is at least t and at most that key, and equal to it when the bucket holds a single
+// value, as on rows of tied values. Valid in lane 63; 0 stays 0.
+__device__ __forceinline__ uint32_t bucket_floor(uint32_t lo, uint32_t t) {
+    const uint32_t m = ~wave_incl_max(t && (lo >> 16) == (t >> 16) ? ~lo : 0u);
+    return t ? m : 0u;
+}
+
 // R for a row of `waves` wavefronts of which at least `waves / share` contribute
 __device__ __forceinline__ uint32_t bound_rank(uint32_t k, int64_t waves, int share) {
     const int64_t r = waves > 0 ? ((int64_t)share * k + waves - 1) / waves : 64;
@@ -696,6 +704,68 @@ __global__ __launch_bounds__(NT) void select_small_kernel(SelectArgs a) {
     const uint32_t k = (uint32_t)a.k;
     uint64_t T = 1ull;  // every candidate
     uint32_t cnt;
+    // Too many candidates: most of them tie (rows of equal values, a zero query). Each round
+    // takes M, the smallest candidate's key, and counts the values strictly above it. Fewer than k
+    // above it: M is the k-th value, and the winners are every value above it and the first ones
+    // equal to it in slot order. Otherwise the next round looks at the values above M. A row left
+    // unresolved (more levels of ties, or few enough values above M) takes the register passes.
+    // The rounds keep their own copies so that the common path below stays as it is.
+    if (__builtin_expect(C > (uint32_t)kCap && T0 != 0u, 0)) {
+        float fL = fT;
+        uint32_t exL = ex, totL = tot;
+        for (int round = 0; round < 3; ++round) {
+            uint32_t mk = 0xffffffffu;
+#pragma unroll
+            for (int r = 0; r < kRuns; ++r)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (v[r][e] >= fL) mk = min(mk, order_key(v[r][e]));
+            const uint32_t wmax = wave_incl_max(~mk);  // the minimum as the maximum of complements
+            if (lane == 63) S.R.red[0][w] = wmax;
+            __syncthreads();
+            uint32_t nmin = 0u;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) nmin = S.R.red[0][i] > nmin ? S.R.red[0][i] : nmin;
+            const uint32_t M = ~nmin;
+            const float fM = key_value(M);
+            uint32_t gr[kRuns];
+#pragma unroll
+            for (int r = 0; r < kRuns; ++r) {
+                gr[r] = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) gr[r] += v[r][e] > fM ? 1u : 0u;
+            }
+            uint32_t totg;
+            const uint32_t exg = block_scan<NT>(gr[0] | (gr[1] << 16), S.R.wsum[(round + 1) & 1], totg);
+            const uint32_t Cg = (totg & 0xffffu) + (totg >> 16);
+            if (Cg < k) {
+                const uint32_t m = k - Cg;
+                uint32_t gb[kRuns] = {exg & 0xffffu, (totg & 0xffffu) + (exg >> 16)};
+                uint32_t tb[kRuns] = {(exL & 0xffffu) - (exg & 0xffffu),
+                                      ((totL & 0xffffu) - (totg & 0xffffu)) + (exL >> 16) - (exg >> 16)};
+#pragma unroll
+                for (int r = 0; r < kRuns; ++r)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint64_t c = composite(order_key(v[r][e]), pb[r] + (uint32_t)e);
+                        if (v[r][e] > fM) {
+                            write_one(a, t, (int)(gb[r] + (tb[r] < m ? tb[r] : m)), c);
+                            ++gb[r];
+                        } else if (v[r][e] >= fL) {
+                            if (tb[r] < m) write_one(a, t, (int)(gb[r] + tb[r]), c);
+                            ++tb[r];
+                        }
+                    }
+                write_pad(a, t, k);
+                return;
+            }
+            if (Cg <= (uint32_t)kCap) break;
+            fL = key_value(M + 1u);
+            exL = exg;
+            totL = totg;
+        }
+        __syncthreads();
+    }
     if (C <= (uint32_t)kCap) {
         uint32_t o[kRuns] = {ex & 0xffffu, (tot & 0xffffu) + (ex >> 16)};
 #pragma unroll
@@ -797,6 +867,7 @@ struct WsView {
     RowState* st;       // [nq]
     ChunkBound* bound;  // [nq][chunks]
     uint64_t* cand;     // [nq][cap]
+    uint32_t* ties;     // [nq][chunks * kChunk / 32]: pool rows' values equal to the bound, as bits
     int64_t cap;
     int64_t chunks;
 };
@@ -811,6 +882,8 @@ __host__ __device__ inline WsView ws_view(void* ws, int32_t nq, int64_t cap) {
     v.bound = (ChunkBound*)p;
     p += align_up((size_t)nq * (size_t)v.chunks * sizeof(ChunkBound));
     v.cand = (uint64_t*)p;
+    p += align_up((size_t)nq * (size_t)v.cap * 8);
+    v.ties = (uint32_t*)p;
     return v;
 }
 
@@ -826,10 +899,12 @@ __global__ __launch_bounds__(kLargeThreads) void select_bound_kernel(SelectArgs 
     chunk_load<kLargeThreads>(a, t, ri, c0, v, pb);
     const uint32_t lm = lane_max(v);
     const int64_t chunks = (ri.len + kChunk - 1) / kChunk;
-    const uint32_t t1 = wave_rth(lm, bound_rank((uint32_t)a.k, chunks * NW, 1));
-    const uint32_t t2 = wave_rth(lm, bound_rank((uint32_t)a.k, chunks * NW, 2));
+    // bucket floors: a row whose values tie at the bound then has the tied key itself as its bound
+    // (the finishing block resolves such ties by position without a radix pass)
+    const uint32_t t1 = bucket_floor(lm, wave_rth(lm, bound_rank((uint32_t)a.k, chunks * NW, 1)));
+    const uint32_t t2 = bucket_floor(lm, wave_rth(lm, bound_rank((uint32_t)a.k, chunks * NW, 2)));
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (lane == 0) {
+    if (lane == 63) {
         wt[0][w] = t1;
         wt[1][w] = t2;
     }
@@ -905,11 +980,32 @@ __global__ __launch_bounds__(kLargeThreads) void select_collect_kernel(SelectArg
     const uint32_t T0 = row_bound<kLargeThreads>(a, ws, t, chunks, red);
     if (blockIdx.x == 0 && threadIdx.x == 0) ws.st[t].t0 = T0;
     const float fT = T0 ? key_value(T0) : -__FLT_MAX__;
+    // Pool rows (block maxima) keep the values equal to the bound out of the list, as bits by block
+    // id: on rows of tied maxima (a zero query) the list stays short, and the finishing block takes
+    // the ties it needs by block id. The chunk's words are written whole, ties or not.
+    const bool split = a.pool_mode && T0 != 0u;
     uint32_t c = 0;
+    uint32_t tm[kRuns] = {0u, 0u};
 #pragma unroll
     for (int r = 0; r < kRuns; ++r)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) c += v[r][e] >= fT ? 1u : 0u;
+        for (int e = 0; e < 8; ++e) {
+            const bool tie = split && v[r][e] == fT;  // -0 is +0 and NaN never equal: the key equals T0
+            tm[r] |= (tie ? 1u : 0u) << e;
+            c += v[r][e] >= fT && !tie ? 1u : 0u;
+        }
+    if (split) {
+        // run r of thread tid is byte tid % 4 of word (c0 + 8 (tid + r NT)) / 32: four lanes per word
+        const int tid = threadIdx.x;
+        uint32_t* trow = ws.ties + t * ws.chunks * (kChunk / 32);
+#pragma unroll
+        for (int r = 0; r < kRuns; ++r) {
+            uint32_t wb = tm[r] << (8 * (tid & 3));
+            wb |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wb, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+            wb |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wb, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+            if ((tid & 3) == 0) trow[(c0 + 8 * (tid + r * kLargeThreads)) >> 5] = wb;
+        }
+    }
     uint32_t tot;
     uint32_t o = block_scan<kLargeThreads>(c, wsum, tot);
     if (threadIdx.x == 0) base = tot ? atomicAdd(&ws.st[t].n_cand, tot) : 0u;
@@ -919,7 +1015,7 @@ __global__ __launch_bounds__(kLargeThreads) void select_collect_kernel(SelectArg
     for (int r = 0; r < kRuns; ++r)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            if (v[r][e] >= fT) out[o++] = list_entry(v[r][e], pb[r] + (uint32_t)e);
+            if (v[r][e] >= fT && !((tm[r] >> e) & 1u)) out[o++] = list_entry(v[r][e], pb[r] + (uint32_t)e);
 }
 
 __global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(SelectArgs a, WsView ws) {
@@ -943,15 +1039,47 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(SelectArg
         L = list;
     }
     __syncthreads();
-    const uint64_t T = C > k ? list_radix<kFinishThreads>(L, C, k, T0, hist, S) : 1ull;
+    // Pool rows with fewer than k list entries above the bound (T0 != 0): the bound is the k-th
+    // value, and the winners are every list entry and the first k - C values equal to the bound,
+    // taken by block id from the tie bitmap the collecting blocks wrote.
+    const bool ties = bitmap && T0 != 0u && C < k;
+    if (ties) {
+        for (uint32_t i = threadIdx.x; i < C; i += kFinishThreads) {
+            const uint32_t pos = comp_pos(entry_composite(L[i]));
+            atomicOr(&bits[pos >> 5], 1u << (pos & 31));
+        }
+        const uint32_t* trow = ws.ties + t * ws.chunks * (kChunk / 32);
+        const uint32_t m = k - C;
+        const int per = (words + kFinishThreads - 1) / kFinishThreads;
+        const int w0 = threadIdx.x * per;
+        uint32_t mine = 0;
+        for (int q = 0; q < per; ++q)
+            if (w0 + q < words) mine += (uint32_t)__popc(trow[w0 + q]);
+        uint32_t nt;
+        uint32_t base = block_scan<kFinishThreads>(mine, S.wsum[1], nt);  // also orders the ORs above
+        for (int q = 0; q < per && w0 + q < words && base < m; ++q) {
+            uint32_t b = trow[w0 + q];
+            const uint32_t c = (uint32_t)__popc(b);
+            if (base + c > m) {  // keep the lowest m - base bits
+                for (uint32_t drop = base + c - m; drop; --drop) b &= ~(1u << (31 - __clz(b)));
+            }
+            atomicOr(&bits[w0 + q], b);
+            base += c;
+        }
+        __syncthreads();
+    }
+    const uint64_t T = (!ties && C > k) ? list_radix<kFinishThreads>(L, C, k, T0, hist, S) : 1ull;
     if (bitmap) {
         // the winners are the entries at or above T: exactly min(C, k) of them, since T is the
-        // k-th largest of distinct composites (or 1, every entry, when C <= k)
-        for (uint32_t i = threadIdx.x; i < C; i += kFinishThreads) {
-            const uint64_t x = entry_composite(L[i]);
-            if (x >= T) {
-                const uint32_t pos = comp_pos(x);
-                atomicOr(&bits[pos >> 5], 1u << (pos & 31));
+        // k-th largest of distinct composites (or 1, every entry, when C <= k); with ties they are
+        // in the bitmap already
+        if (!ties) {
+            for (uint32_t i = threadIdx.x; i < C; i += kFinishThreads) {
+                const uint64_t x = entry_composite(L[i]);
+                if (x >= T) {
+                    const uint32_t pos = comp_pos(x);
+                    atomicOr(&bits[pos >> 5], 1u << (pos & 31));
+                }
             }
         }
         __syncthreads();
@@ -974,7 +1102,7 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(SelectArg
                 ++base;
             }
         }
-        write_pad(a, t, C < k ? C : k);
+        write_pad(a, t, ties ? k : (C < k ? C : k));
         return;
     }
     // the winners, gathered in rounds of 8 consecutive entries per thread
@@ -1032,7 +1160,7 @@ size_t select_workspace_bytes(int32_t nq, int64_t cap, int32_t k) {
     if (cap <= kSmallRow) return 256;
     const WsView v = ws_view(nullptr, nq, cap);
     return align_up((size_t)nq * sizeof(RowState)) + align_up((size_t)nq * (size_t)v.chunks * sizeof(ChunkBound)) +
-           align_up((size_t)nq * (size_t)v.cap * 8);
+           align_up((size_t)nq * (size_t)v.cap * 8) + align_up((size_t)nq * (size_t)v.chunks * (kChunk / 32) * 4);
 }
 
 size_t select_counter_bytes(int32_t nq) { return nq > 0 ? (size_t)nq * sizeof(RowState) : 0; }
