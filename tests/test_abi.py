@@ -260,6 +260,37 @@ def test_topk_pool_validation(fx):
     assert m(*bad) == fx.IDX_EUNSUPPORTED
 
 
+def test_recorded_calls_replay_in_order_and_raise_on_failure(fx):
+    """record() keeps the binding's library calls without running them; Recorded replays them
+    in order and raises the library's status like a direct call"""
+    seen = []
+
+    def fake(status):
+        def f(*args):
+            seen.append((status, args))
+            return status
+        return f
+
+    ok, bad = fake(fx.IDX_OK), fake(fx.IDX_EINVAL)
+    with fx.record() as calls:
+        fx._call(ok, 1, 2)
+        fx._call(ok, 3)
+    assert seen == [] and [c[1] for c in calls] == [(1, 2), (3,)]
+    rep = fx.Recorded(calls)
+    rep()
+    rep()
+    assert seen == [(0, (1, 2)), (0, (3,)), (0, (1, 2)), (0, (3,))]
+    with pytest.raises(fx.IdxError):
+        fx.Recorded([(ok, (5,)), (bad, (6,)), (ok, (7,))])()
+    assert seen[-2:] == [(0, (5,)), (fx.IDX_EINVAL, (6,))]  # stops at the failing call
+    with pytest.raises(RuntimeError):
+        with fx.record():
+            with fx.record():
+                pass
+    fx._call(ok, 9)  # recording ended with the failed nesting: calls run again
+    assert seen[-1] == (0, (9,))
+
+
 def test_python_binding_refuses_cpu_tensors(fx):
     import torch
 

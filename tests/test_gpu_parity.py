@@ -401,6 +401,23 @@ def test_gather_long_form_lists(fx, nq, max_blocks, stride):
     assert np.array_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32))
 
 
+def test_recorded_decode_step_equals_run(fx, pl):
+    """DecodePlan.compiled(): the recorded step, replayed twice, leaves every output equal to run()'s"""
+    wl = synth.decode_workload("rec", 77, [30000, 3001, 100000], layers=2)
+    dev = pl.DeviceWorkload.from_workload(wl)
+    a = pl.DecodePlan(dev)
+    a.run()
+    b = pl.DecodePlan(dev)
+    rep = b.compiled()
+    rep()
+    rep()
+    torch.cuda.synchronize()
+    assert torch.equal(a.pool_blocks, b.pool_blocks) and torch.equal(a.pool_count, b.pool_count)
+    for layer in range(a.layers + 1):
+        assert torch.equal(a.topk[layer], b.topk[layer])
+        assert torch.equal(a.topk_val[layer], b.topk_val[layer])
+
+
 def check_decode(fx, pl, wl, k=512):
     dev = pl.DeviceWorkload.from_workload(wl)
     out = pl.decode_step(dev, k=k)

@@ -7,6 +7,7 @@ CPU or eager fallback: importing fails if the library has not been built.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -61,6 +62,47 @@ class IdxError(RuntimeError):
 def _check(status: int) -> None:
     if status != IDX_OK:
         raise IdxError(status, lib.idx_last_error().decode())
+
+
+_recording: list | None = None
+
+
+def _call(fn, *args) -> None:
+    """Run one library call and raise on a failed status, or, inside record(), only keep it."""
+    if _recording is not None:
+        _recording.append((fn, args))
+        return
+    _check(fn(*args))
+
+
+class Recorded:
+    """A fixed sequence of library calls with their arguments marshalled once (tensor checks,
+    pointers, strides and the stream resolved when recorded): replaying costs the host one foreign
+    call per launch. The tensors the calls name must keep their storage while it is in use."""
+
+    def __init__(self, calls: list):
+        self.calls = list(calls)
+
+    def __call__(self) -> None:
+        for fn, args in self.calls:
+            status = fn(*args)
+            if status != IDX_OK:
+                raise IdxError(status, lib.idx_last_error().decode())
+
+
+@contextlib.contextmanager
+def record():
+    """Collect the library calls made inside the block, without running them: yields a list that
+    holds them afterwards (wrap it in Recorded to replay)."""
+    global _recording
+    if _recording is not None:
+        raise RuntimeError("record() does not nest")
+    calls: list = []
+    _recording = calls
+    try:
+        yield calls
+    finally:
+        _recording = None
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:
@@ -122,7 +164,7 @@ def idx_quantize_q(x: torch.Tensor, signs: torch.Tensor, codes: torch.Tensor | N
         codes = torch.empty(*lead, 64, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(*lead, 4, dtype=torch.uint8, device=x.device)
-    _check(lib.idx_quantize_q(_ptr(x), rows, _ptr(signs), _ptr(codes), _ptr(scales), _stream(stream)))
+    _call(lib.idx_quantize_q, _ptr(x), rows, _ptr(signs), _ptr(codes), _ptr(scales), _stream(stream))
     return codes, scales
 
 
@@ -135,10 +177,10 @@ def idx_score_full(k_codes, k_scales, k_base, n_vis, q_codes, q_scales, w, max_n
     _need(w, torch.float32, "w")
     ss = scores.stride(0) if scores is not None else (head_dots.shape[-1] if head_dots is not None else 0)
     bs = block_max.stride(0) if block_max is not None else 0
-    _check(lib.idx_score_full(_ptr(k_codes), _ptr(k_scales), _ptr(k_base), _ptr(n_vis), nq, group, max_n,
-                              _ptr(q_codes), _ptr(q_scales), _ptr(w),
-                              _ptr(scores) if head_dots is not None else _rows_ptr(scores), ss,
-                              _rows_ptr(block_max), bs, _ptr(head_dots), _stream(stream)))
+    _call(lib.idx_score_full, _ptr(k_codes), _ptr(k_scales), _ptr(k_base), _ptr(n_vis), nq, group, max_n,
+          _ptr(q_codes), _ptr(q_scales), _ptr(w),
+          _ptr(scores) if head_dots is not None else _rows_ptr(scores), ss,
+          _rows_ptr(block_max), bs, _ptr(head_dots), _stream(stream))
     return scores, block_max, head_dots
 
 
@@ -147,9 +189,9 @@ def idx_build_pool(block_max, n_vis, max_n: int, pool_blocks, pool_count, ws, to
     nq = n_vis.shape[0]
     _need(block_max, torch.float32, "block_max")
     _need(pool_blocks, torch.int32, "pool_blocks")
-    _check(lib.idx_build_pool(_rows_ptr(block_max), block_max.stride(0), _ptr(n_vis), nq, max_n, topk_blocks, block,
-                              _ptr(pool_blocks), pool_blocks.stride(0), _ptr(pool_count), _ptr(ws), ws.numel(),
-                              _stream(stream)))
+    _call(lib.idx_build_pool, _rows_ptr(block_max), block_max.stride(0), _ptr(n_vis), nq, max_n, topk_blocks, block,
+          _ptr(pool_blocks), pool_blocks.stride(0), _ptr(pool_count), _ptr(ws), ws.numel(),
+          _stream(stream))
     return pool_blocks, pool_count
 
 
@@ -159,9 +201,9 @@ def idx_build_pool_noalloc(block_max, n_vis, max_n: int, pool_blocks, pool_count
     nq = n_vis.shape[0]
     _need(block_max, torch.float32, "block_max")
     _need(pool_blocks, torch.int32, "pool_blocks")
-    _check(lib.idx_build_pool_noalloc(_rows_ptr(block_max), block_max.stride(0), _ptr(n_vis), nq, max_n, topk_blocks,
-                                      block, _ptr(pool_blocks), pool_blocks.stride(0), _ptr(pool_count),
-                                      _stream(stream)))
+    _call(lib.idx_build_pool_noalloc, _rows_ptr(block_max), block_max.stride(0), _ptr(n_vis), nq, max_n, topk_blocks,
+          block, _ptr(pool_blocks), pool_blocks.stride(0), _ptr(pool_count),
+          _stream(stream))
     return pool_blocks, pool_count
 
 
@@ -170,8 +212,8 @@ def idx_top_blocks(block_max, n_vis, max_n: int, k: int, blocks, count, ws, bloc
     nq = n_vis.shape[0]
     _need(block_max, torch.float32, "block_max")
     _need(blocks, torch.int32, "blocks")
-    _check(lib.idx_top_blocks(_rows_ptr(block_max), block_max.stride(0), _ptr(n_vis), nq, max_n, k, block,
-                              _rows_ptr(blocks), blocks.stride(0), _ptr(count), _ptr(ws), ws.numel(), _stream(stream)))
+    _call(lib.idx_top_blocks, _rows_ptr(block_max), block_max.stride(0), _ptr(n_vis), nq, max_n, k, block,
+          _rows_ptr(blocks), blocks.stride(0), _ptr(count), _ptr(ws), ws.numel(), _stream(stream))
     return blocks, count
 
 
@@ -179,12 +221,12 @@ def idx_score_pool_gather(k_codes, k_scales, k_base, n_vis, blocks, block_count,
                           q_scales, w, scores, head_dots=None, block: int = BLOCK, stream=None):
     nq = n_vis.shape[0]
     _need(scores, torch.float32, "scores")
-    _check(lib.idx_score_pool_gather(_ptr(k_codes), _ptr(k_scales), _ptr(k_base), _ptr(n_vis), nq, _rows_ptr(blocks),
-                                     blocks.stride(0), _ptr(block_count), max_blocks, block, _ptr(q_codes),
-                                     _ptr(q_scales), _ptr(w),
-                                     _ptr(scores) if head_dots is not None else _rows_ptr(scores), scores.stride(0),
-                                     _ptr(head_dots),
-                                     _stream(stream)))
+    _call(lib.idx_score_pool_gather, _ptr(k_codes), _ptr(k_scales), _ptr(k_base), _ptr(n_vis), nq, _rows_ptr(blocks),
+          blocks.stride(0), _ptr(block_count), max_blocks, block, _ptr(q_codes),
+          _ptr(q_scales), _ptr(w),
+          _ptr(scores) if head_dots is not None else _rows_ptr(scores), scores.stride(0),
+          _ptr(head_dots),
+          _stream(stream))
     return scores
 
 
@@ -193,9 +235,9 @@ def idx_topk(scores, max_n: int, k: int, out_idx, ws, n_valid=None, out_val=None
     nq = scores.shape[0]
     _need(scores, torch.float32, "scores")
     _need(out_idx, torch.int32, "out_idx")
-    _check(lib.idx_topk(_rows_ptr(scores), scores.stride(0), _ptr(n_valid), nq, max_n, k, _rows_ptr(blocks),
-                        blocks.stride(0) if blocks is not None else 0, block, _ptr(out_idx), out_idx.stride(0),
-                        _ptr(out_val), _ptr(ws), ws.numel(), _stream(stream)))
+    _call(lib.idx_topk, _rows_ptr(scores), scores.stride(0), _ptr(n_valid), nq, max_n, k, _rows_ptr(blocks),
+          blocks.stride(0) if blocks is not None else 0, block, _ptr(out_idx), out_idx.stride(0),
+          _ptr(out_val), _ptr(ws), ws.numel(), _stream(stream))
     return out_idx, out_val
 
 
@@ -209,7 +251,7 @@ def idx_quantize_kv(x: torch.Tensor, codes: torch.Tensor | None = None, scales: 
         codes = torch.empty(*lead, MKV_DIM // 2, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(*lead, MKV_DIM // 16, dtype=torch.uint8, device=x.device)
-    _check(lib.idx_quantize_kv(_ptr(x), rows, _ptr(codes), _ptr(scales), _stream(stream)))
+    _call(lib.idx_quantize_kv, _ptr(x), rows, _ptr(codes), _ptr(scales), _stream(stream))
     return codes, scales
 
 
@@ -223,8 +265,8 @@ def idx_gather_kv(codes, scales, kv_base, n_vis, idx, out=None, k: int | None = 
     if out is None:
         out = torch.empty(nq, k, MKV_DIM, dtype=torch.bfloat16, device=idx.device)
     _need(out, torch.bfloat16, "out")
-    _check(lib.idx_gather_kv(_ptr(codes), _ptr(scales), _ptr(kv_base), _ptr(n_vis), nq, _ptr(idx), idx.stride(0), k,
-                             _ptr(out), _stream(stream)))
+    _call(lib.idx_gather_kv, _ptr(codes), _ptr(scales), _ptr(kv_base), _ptr(n_vis), nq, _ptr(idx), idx.stride(0), k,
+          _ptr(out), _stream(stream))
     return out
 
 
@@ -235,8 +277,8 @@ def idx_mask_pool(scores, n_vis, max_n: int, pool_blocks, pool_count, group: int
     _need(scores, torch.float32, "scores")
     _need(pool_blocks, torch.int32, "pool_blocks")
     nq = n_vis.shape[0]
-    _check(lib.idx_mask_pool(_rows_ptr(scores), scores.stride(0), _ptr(n_vis), nq, max_n, _rows_ptr(pool_blocks),
-                             pool_blocks.stride(0), _ptr(pool_count), group, block, _stream(stream)))
+    _call(lib.idx_mask_pool, _rows_ptr(scores), scores.stride(0), _ptr(n_vis), nq, max_n, _rows_ptr(pool_blocks),
+          pool_blocks.stride(0), _ptr(pool_count), group, block, _stream(stream))
     return scores
 
 
@@ -248,7 +290,7 @@ def idx_topk_pool(scores, n_vis, max_n: int, pool_blocks, pool_count, max_blocks
     _need(pool_blocks, torch.int32, "pool_blocks")
     _need(out_idx, torch.int32, "out_idx")
     nq = n_vis.shape[0]
-    _check(lib.idx_topk_pool(_rows_ptr(scores), scores.stride(0), _ptr(n_vis), nq, max_n, _rows_ptr(pool_blocks),
-                             pool_blocks.stride(0), _ptr(pool_count), max_blocks, group, block, k, _ptr(out_idx),
-                             out_idx.stride(0), _ptr(out_val), _stream(stream)))
+    _call(lib.idx_topk_pool, _rows_ptr(scores), scores.stride(0), _ptr(n_vis), nq, max_n, _rows_ptr(pool_blocks),
+          pool_blocks.stride(0), _ptr(pool_count), max_blocks, group, block, k, _ptr(out_idx),
+          out_idx.stride(0), _ptr(out_val), _stream(stream))
     return out_idx, out_val

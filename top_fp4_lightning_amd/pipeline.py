@@ -36,8 +36,8 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from . import (BLOCK, IDX_OP_BUILD_POOL, IDX_OP_TOPK, idx_build_pool, idx_mask_pool, idx_quantize_q,
-               idx_score_full, idx_score_pool_gather, idx_top_blocks, idx_topk, idx_topk_pool, workspace)
+from . import (BLOCK, IDX_OP_BUILD_POOL, IDX_OP_TOPK, Recorded, idx_build_pool, idx_mask_pool, idx_quantize_q,
+               idx_score_full, idx_score_pool_gather, idx_top_blocks, idx_topk, idx_topk_pool, record, workspace)
 
 
 @dataclass
@@ -146,6 +146,13 @@ class DecodePlan:
             self.quantize(layer, stream)
             self.pool_select(layer, stream)
         return self
+
+    def compiled(self, stream=None) -> Recorded:
+        """The step of run() recorded once: replaying it issues the same launches on the same
+        stream without marshalling each call again on the host."""
+        with record() as calls:
+            self.run(stream)
+        return Recorded(calls)
 
 
 class TokenPlan:
