@@ -512,8 +512,10 @@ constexpr uint32_t kInfKey = 0xff800000u;  // order key of +inf
 // T for the candidates L[0 .. C) (C > k, at least k of them with keys >= T0); hist holds two
 // 2048-bin scratch histograms (passes alternate between them, so that clearing the next one
 // needs no barrier of its own). Called by the whole block; contains barriers. +inf entries (the
-// pinned block, +inf values) are counted first and kept out of the passes, so that the first
-// digit starts below the bits shared by T0 and the largest finite key.
+// pinned block, +inf values) are counted first and kept out of the passes. Each pass splits the
+// composite range [rlo, rhi) that holds the threshold into 2048 equal bins of 2^sh (the first
+// range runs from T0 to the largest finite key, so that its bins spread the candidates thinly);
+// a bin whose entries all win ends the search, and a bin of at most 64 entries is ranked directly.
 template <int NT>
 __device__ uint64_t list_radix(const uint64_t* L, uint32_t C, uint32_t k, uint32_t T0, uint32_t* hist,
                                RadixShared<NT>& S) {
@@ -551,30 +553,25 @@ __device__ uint64_t list_radix(const uint64_t* L, uint32_t C, uint32_t k, uint32
         ni += S.red[1][i];
     }
     uint32_t need = k;
-    int hi;
-    uint64_t mask, prefix, lim;
-    if (ni >= need) {  // the threshold lies among the +inf entries: positions decide
-        hi = 31;
-        mask = 0xffffffff00000000ull;
-        prefix = (uint64_t)kInfKey << 32;
-        lim = ~0ull;
+    uint64_t rlo, rhi;  // the threshold composite lies in [rlo, rhi)
+    if (ni >= need) {   // among the +inf entries: positions decide
+        rlo = (uint64_t)kInfKey << 32;
+        rhi = rlo + (1ull << 32);
     } else {
         need -= ni;
-        const uint32_t dk = T0 ^ km;
-        hi = dk ? 63 - __clz(dk) : 31;
-        mask = hi >= 63 ? 0ull : ~((1ull << (hi + 1)) - 1ull);
-        prefix = ((uint64_t)T0 << 32) & mask;
-        lim = (uint64_t)kInfKey << 32;
+        rlo = (uint64_t)T0 << 32;
+        rhi = ((uint64_t)km + 1ull) << 32;  // km < kInfKey: no overflow
     }
     int sb = 0;
     for (int pass = 0;; ++pass) {
-        const int width = hi + 1 < 11 ? hi + 1 : 11;
-        const int lo = hi - width + 1;
-        const uint64_t dm = (1ull << width) - 1ull;
+        // the fewest bits per bin that cover the range with 2048 bins
+        const uint64_t span1 = rhi - rlo - 1ull;
+        const int bits = span1 ? 64 - __clzll((long long)span1) : 0;
+        const int sh = bits > 11 ? bits - 11 : 0;
         uint32_t* h = hist + (pass & 1) * kHistBins;
         for (uint32_t i = tid; i < C; i += NT) {
             const uint64_t x = entry_composite(L[i]);
-            if (((x ^ prefix) & mask) == 0 && x < lim) bin_add(h, (uint32_t)((x >> lo) & dm));
+            if (x >= rlo && x < rhi) bin_add(h, (uint32_t)((x - rlo) >> sh));
         }
         __syncthreads();
         // every thread is past the previous pass's reads of the other histogram: clear it for
@@ -607,17 +604,18 @@ __device__ uint64_t list_radix(const uint64_t* L, uint32_t C, uint32_t k, uint32
         const int d = S.digit;
         const uint32_t above = S.above;
         const uint32_t on = h[d];
-        if (on == need - above) return prefix | ((uint64_t)d << lo);
+        const uint64_t blo = rlo + ((uint64_t)d << sh);
+        if (on == need - above) return blo;
         need -= above;
-        prefix |= (uint64_t)d << lo;
-        mask |= dm << lo;
-        hi = lo - 1;
-        if (on <= 64 || hi < 0) break;
+        const uint64_t bhi = blo + (1ull << sh);  // blo < rhi <= 0xff80000100000000, sh <= 53: no overflow
+        rlo = blo;
+        rhi = bhi < rhi ? bhi : rhi;
+        if (on <= 64 || sh == 0) break;
     }
-    // the few elements on the digit, ranked against each other (counters cleared at the start)
+    // the few elements in the bin, ranked against each other (counters cleared at the start)
     for (uint32_t i = tid; i < C; i += NT) {
         const uint64_t x = entry_composite(L[i]);
-        if (((x ^ prefix) & mask) == 0 && x < lim) {
+        if (x >= rlo && x < rhi) {
             const uint32_t f = atomicAdd(&S.nfin, 1u);
             if (f < 64u) S.fin[f] = x;
         }
