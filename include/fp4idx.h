@@ -130,6 +130,9 @@ idx_status idx_quantize_q(const uint16_t* x_bf16, int64_t rows, const int8_t* si
  * Rows written by idx_quantize_q from activations have group exponents within a few units of each
  * other (the rotation spreads a row's energy over all four groups); the seeded workloads of this
  * library never exceed a spread of 9.
+ * Summation order. Scores, and block maxima computed alongside scores, are bit-identical across
+ * group values and with idx_score_pool_gather. Block maxima requested without scores at group > 1
+ * sum the same exact per-head terms in another fp32 order (within the same tolerance).
  */
 idx_status idx_score_full(const uint8_t* k_codes, const uint8_t* k_scales, const int64_t* k_base,
                           const int32_t* n_vis, int32_t nq, int32_t group, int64_t max_n, const uint8_t* q_codes,

@@ -18,9 +18,13 @@ namespace {
 // (j = 0..15). On this chip a 32x32x64 op overlaps the ReLU epilogue better than two
 // 16x16x128 ops and leaves half the matrix instructions.
 //
-// The head sum is taken in the same order as the single-query scan, so both paths give
-// bit-identical scores: each lane keeps the two 8-head chains (4g .. 4g+3, 16+4g .. 16+4g+3)
-// for g = l / 32 and g + 2, adds them, and one cross-half add completes the key.
+// When scores are written, the head sum is taken in the same order as the single-query scan, so
+// both paths give bit-identical scores: each lane keeps the two 8-head chains (4g .. 4g+3,
+// 16+4g .. 16+4g+3) for g = l / 32 and g + 2, adds them, and one cross-half add completes the key.
+// The block-maxima-only form (chunked prefill, speculative verification) sums a lane's 16 heads
+// in one chain instead: one vector instruction fewer per tile on a kernel bound by vector issue,
+// and a different rounding of the same exact per-head dots (fp32 sums of 32 terms, well inside the
+// scores' 1e-5 tolerance).
 //
 // Each wave keeps QW queries in registers and applies every tile it loads to all of them; the
 // four waves of a block take consecutive queries and the same key chunk. Grid: x = query tiles
@@ -66,17 +70,26 @@ __device__ __forceinline__ v16f mfma_tile32(const QRegs32& q, const KTile32& kt)
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(q.a[1]), widen(kt.b[1]), t, 4, 4, 1, q.sc, 1, kt.sc);
 }
 
-// this lane's partial: chain over rows j = 0-3, 8-11 plus chain over rows 4-7, 12-15
+// this lane's partial. SAME_ORDER: chain over rows j = 0-3, 8-11 plus chain over rows 4-7, 12-15
+// (the single-query scan's order); otherwise one chain over the 16 rows
+template <bool SAME_ORDER>
 __device__ __forceinline__ float lane_partial32(const QRegs32& q, const v16f& o) {
-    float pa = 0.0f, pb = 0.0f;
+    if constexpr (SAME_ORDER) {
+        float pa = 0.0f, pb = 0.0f;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pa = fmaf(q.w[8 * b + i], relu(o[8 * b + i]), pa);
-            pb = fmaf(q.w[8 * b + 4 + i], relu(o[8 * b + 4 + i]), pb);
-        }
-    return pa + pb;
+            for (int i = 0; i < 4; ++i) {
+                pa = fmaf(q.w[8 * b + i], relu(o[8 * b + i]), pa);
+                pb = fmaf(q.w[8 * b + 4 + i], relu(o[8 * b + 4 + i]), pb);
+            }
+        return pa + pb;
+    } else {
+        float p = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) p = fmaf(q.w[j], relu(o[j]), p);
+        return p;
+    }
 }
 
 // two tiles' partials -> in lane l the score of key l of the 64-key step
@@ -243,7 +256,7 @@ __global__ __launch_bounds__(256) void score_multi_kernel(ScoreArgs a) {
             if (i >= qv) break;  // uniform per wave
             const v16f o0 = mfma_tile32(q[i], t[0]);
             const v16f o1 = mfma_tile32(q[i], t[1]);
-            const float sc = combine2(lane_partial32(q[i], o0), lane_partial32(q[i], o1));
+            const float sc = combine2(lane_partial32<SCORES>(q[i], o0), lane_partial32<SCORES>(q[i], o1));
             const bool valid = !MASKED || el < nq_[i];
             if (SCORES)
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), sc_rsrc[i], sc_voff, it * kStepKeys * 4, 0);
