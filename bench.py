@@ -813,7 +813,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="fullscan_1m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config-reps", type=int, default=10,
