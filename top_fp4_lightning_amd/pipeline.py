@@ -173,6 +173,12 @@ class TokenPlan:
         self.decoder.run(stream)
         return self
 
+    def compiled(self, stream=None) -> Recorded:
+        """The token of run() recorded once (as DecodePlan.compiled)."""
+        with record() as calls:
+            self.run(stream)
+        return Recorded(calls)
+
 
 def decode_step(dev: DeviceWorkload, plan: DecodePlan | None = None, **kw) -> dict:
     plan = plan or DecodePlan(dev, **kw)
